@@ -1,0 +1,327 @@
+"""CPU oracle for ProxyAttn block-sparse causal prefill attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path (the
+HIP library and its Python binding) never does and shares no code with it.
+
+Plain, slow, float64 NumPy.  Each function follows one step of the method as
+the ProxyAttn blog post (ir.hit.edu.cn, "ProxyAttn ... ICLR 2026") describes
+it, in the order of its section 4 ("ProxyAttn方法详解"):
+
+  step 1 / Head Pooling       -> proxy_pool
+  step 1 / Score Estimation   -> proxy_scores
+  step 1 / Block Ranking      -> rank_blocks
+  step 2 / dynamic budget     -> last_block_masses, budget_from_masses
+  final sparse mask           -> select_blocks
+  FlashAttention on the mask  -> sparse_attention
+
+Readings taken where the pages leave a step open (each is stated again in the
+function that applies it):
+
+* pooling is the arithmetic mean over a group's query heads (Q) and over the
+  distinct KV heads those query heads use (K);
+* token-level score = scale * q.k logit (no softmax), causal entries only;
+  blocks above the diagonal are -inf and never selectable;
+* the proxies are stored as bfloat16 and the block scores as float32: the
+  ranking is an integer decision, so it is taken on the values in the
+  precision the GPU path stores them in (round-to-nearest-even);
+* ranking order: score descending, block index ascending on ties;
+* budget: the last query block's exact causal softmax, averaged over its
+  queries, summed per key block, accumulated (float64) along the group's
+  ranking of the last row; k_h = first count whose cumulative mass >= gamma,
+  else nb;
+* selection: row I keeps the first min(k_h, I+1) blocks of its ranking plus
+  the diagonal block I;
+* output: exact softmax renormalised over the kept causal keys.
+
+parity: pinned (tests/test_oracle_pins.py, tests/test_golden.py).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# --------------------------------------------------------------------------
+# head bookkeeping
+# --------------------------------------------------------------------------
+def kv_head_of(h: int, H: int, Hkv: int) -> int:
+    """KV head serving query head h: consecutive query heads share one KV head."""
+    return h // (H // Hkv)
+
+
+def group_of(h: int, H: int, G: int) -> int:
+    """Proxy group of query head h: G equal runs of consecutive heads."""
+    return h // (H // G)
+
+
+def group_query_heads(g: int, H: int, G: int) -> List[int]:
+    n = H // G
+    return list(range(g * n, (g + 1) * n))
+
+
+def group_kv_heads(g: int, H: int, Hkv: int, G: int) -> List[int]:
+    """Distinct KV heads used by the query heads of group g, ascending."""
+    return sorted({kv_head_of(h, H, Hkv) for h in group_query_heads(g, H, G)})
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
+
+    Works on the float64 significand: frexp gives x = m * 2**e with
+    0.5 <= |m| < 1; bfloat16 keeps 8 significant bits, i.e. m to a multiple of
+    2**-8.  numpy's round() is round-half-to-even.  Valid for the normal range
+    (the workloads never reach subnormals or overflow).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
+# --------------------------------------------------------------------------
+# step 1: head pooling
+# --------------------------------------------------------------------------
+def proxy_pool(q: np.ndarray, k: np.ndarray, G: int, to_bf16: bool = True):
+    """Proxy heads: mean of Q over each group's query heads, of K over its KV heads.
+
+    Blog post section 4, step 1 "Head Pooling" (aggregate Q and K over the head
+    dimension inside a group to get one proxy head); section 3 calls it a
+    simple pooling.  Mean is the reading taken (a positive rescaling, so the
+    ranking equals that of a sum).  With to_bf16 the proxies are rounded once
+    to bfloat16, the precision the scores are computed from on the GPU.
+
+    q: [H, N, d], k: [Hkv, N, d] -> qbar, kbar: [G, N, d] float64.
+    """
+    H, N, d = q.shape
+    Hkv = k.shape[0]
+    if H % G or (Hkv % G and G % Hkv):
+        raise ValueError("unsupported grouping")
+    qbar = np.zeros((G, N, d))
+    kbar = np.zeros((G, N, d))
+    for g in range(G):
+        qh = group_query_heads(g, H, G)
+        kh = group_kv_heads(g, H, Hkv, G)
+        qbar[g] = np.mean(np.asarray(q[qh], dtype=np.float64), axis=0)
+        kbar[g] = np.mean(np.asarray(k[kh], dtype=np.float64), axis=0)
+    if to_bf16:
+        qbar, kbar = round_bf16(qbar), round_bf16(kbar)
+    return qbar, kbar
+
+
+# --------------------------------------------------------------------------
+# step 1: score estimation (token-level logits, block max-pool)
+# --------------------------------------------------------------------------
+def proxy_score_row(qbar_g: np.ndarray, kbar_g: np.ndarray, I: int, block: int,
+                    scale: float) -> np.ndarray:
+    """Block scores of query-block row I for one proxy: float64 [I+1].
+
+    Blog post section 4, step 1 "Score Estimation": token-level proxy scores,
+    then a block-level max pool (section 2 fixes the 128x128 block).  Causal
+    prefill: inside the diagonal block only keys j <= i count.
+    """
+    rows = slice(I * block, (I + 1) * block)
+    L = scale * (qbar_g[rows] @ kbar_g[: (I + 1) * block].T)      # [B, (I+1)B]
+    i_idx = np.arange(I * block, (I + 1) * block)[:, None]
+    j_idx = np.arange((I + 1) * block)[None, :]
+    L = np.where(j_idx <= i_idx, L, NEG_INF)
+    return L.reshape(block, I + 1, block).max(axis=(0, 2))
+
+
+def proxy_scores(qbar: np.ndarray, kbar: np.ndarray, block: int = 128,
+                 scale: Optional[float] = None, rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """S[g, I, J] for all proxies: float64 [G, nb, nb], -inf above the diagonal.
+
+    rows: optional subset of query-block rows to fill (others stay -inf).
+    """
+    G, N, d = qbar.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nb = N // block
+    S = np.full((G, nb, nb), NEG_INF)
+    for g in range(G):
+        for I in (range(nb) if rows is None else rows):
+            S[g, I, : I + 1] = proxy_score_row(qbar[g], kbar[g], I, block, scale)
+    return S
+
+
+# --------------------------------------------------------------------------
+# step 1: block ranking
+# --------------------------------------------------------------------------
+def rank_blocks(S_row: np.ndarray, I: int) -> np.ndarray:
+    """Ranking of the causal key blocks J in [0, I] of one row (best first).
+
+    Blog post section 4, step 1 "Block Ranking".  The pages give no tie rule;
+    the reading is: score descending, then block index ascending.  Scores are
+    compared as the float32 values the GPU path stores.
+    """
+    s = np.asarray(S_row[: I + 1], dtype=np.float32).astype(np.float64)
+    J = np.arange(I + 1)
+    return np.lexsort((J, -s))
+
+
+# --------------------------------------------------------------------------
+# step 2: block-aware dynamic budget
+# --------------------------------------------------------------------------
+def last_block_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int,
+                      scale: float) -> np.ndarray:
+    """Mean causal attention mass per key block for the last query block.
+
+    Blog post section 4, step 2: the last small portion of query blocks is
+    used to estimate each head's block-level sparsity.  Reading: the last full
+    block of B queries; each query's exact softmax over its causal keys; the
+    per-block mass is averaged over the B queries (so the masses sum to 1).
+
+    q_h: [N, d] one query head, k_kv: [N, d] its KV head -> m: [nb] float64.
+    """
+    N = q_h.shape[0]
+    nb = N // block
+    T = np.arange(N - block, N)
+    L = scale * (np.asarray(q_h[T], dtype=np.float64) @ np.asarray(k_kv, dtype=np.float64).T)
+    L = np.where(np.arange(N)[None, :] <= T[:, None], L, NEG_INF)
+    L = L - L.max(axis=1, keepdims=True)
+    P = np.exp(L)
+    P /= P.sum(axis=1, keepdims=True)
+    return P.reshape(block, nb, block).sum(axis=2).mean(axis=0)
+
+
+def budget_from_masses(m: np.ndarray, order: np.ndarray, gamma: float) -> int:
+    """k_h: fewest top-ranked blocks whose cumulative mass reaches gamma.
+
+    Blog post section 4, step 2 (per-head block budget over the shared
+    ranking).  The smallest-set-with-cumulative-mass >= threshold rule has the
+    same form as find_blocks in the XAttention report (leeon-k.github.io,
+    section 2.2).  Accumulated in float64; if gamma is never reached the
+    budget is every block (nb).
+    """
+    cum = 0.0
+    for r, J in enumerate(order):
+        cum += float(m[J])
+        if cum >= gamma:
+            return r + 1
+    return len(m)
+
+
+def budgets(q: np.ndarray, k: np.ndarray, S: np.ndarray, G: int, gamma: float,
+            block: int = 128, scale: Optional[float] = None):
+    """k_h for every query head, plus the masses m_h [H, nb].
+
+    The ranking used is that of row nb-1 of the head's group (the same ranking
+    the selection applies to that row).
+    """
+    H, N, d = q.shape
+    Hkv = k.shape[0]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nb = N // block
+    kh = np.zeros(H, dtype=np.int64)
+    masses = np.zeros((H, nb))
+    for h in range(H):
+        g = group_of(h, H, G)
+        order = rank_blocks(S[g, nb - 1], nb - 1)
+        masses[h] = last_block_masses(q[h], k[kv_head_of(h, H, Hkv)], block, scale)
+        kh[h] = budget_from_masses(masses[h], order, gamma)
+    return kh, masses
+
+
+# --------------------------------------------------------------------------
+# final block-sparse mask
+# --------------------------------------------------------------------------
+def select_row(S_row: np.ndarray, I: int, k: int) -> np.ndarray:
+    """Kept key blocks of row I (ascending): top-min(k, I+1) of the ranking plus I."""
+    order = rank_blocks(S_row, I)
+    kept = set(int(J) for J in order[: min(int(k), I + 1)])
+    kept.add(I)
+    return np.array(sorted(kept), dtype=np.int64)
+
+
+def select_blocks(S: np.ndarray, kh: Sequence[int], H: int,
+                  rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Boolean keep mask [H, nb, nb] (rows not listed stay all-False).
+
+    Blog post section 4: the ranking of step 1 and the budgets of step 2 make
+    the final block sparse mask handed to FlashAttention.
+    """
+    G, nb, _ = S.shape
+    keep = np.zeros((H, nb, nb), dtype=bool)
+    for h in range(H):
+        g = group_of(h, H, G)
+        for I in (range(nb) if rows is None else rows):
+            keep[h, I, select_row(S[g, I], I, kh[h])] = True
+    return keep
+
+
+# --------------------------------------------------------------------------
+# block-sparse causal attention
+# --------------------------------------------------------------------------
+def sparse_attention_row(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
+                         blocks: Sequence[int], I: int, block: int, scale: float) -> np.ndarray:
+    """Output rows of query block I attending to the kept key blocks only.
+
+    Standard attention (blog post section 2: softmax-normalised q.k weights
+    applied to v), restricted to the keys of the kept blocks and to j <= i,
+    renormalised over those keys.  Returns [B, d] float64.
+    """
+    qi = np.asarray(q_h[I * block:(I + 1) * block], dtype=np.float64)
+    cols = np.concatenate([np.arange(J * block, (J + 1) * block) for J in blocks])
+    L = scale * (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)
+    i_idx = np.arange(I * block, (I + 1) * block)[:, None]
+    L = np.where(cols[None, :] <= i_idx, L, NEG_INF)
+    L = L - L.max(axis=1, keepdims=True)
+    P = np.exp(L)
+    P /= P.sum(axis=1, keepdims=True)
+    return P @ np.asarray(v_kv[cols], dtype=np.float64)
+
+
+def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
+                     block: int = 128, scale: Optional[float] = None,
+                     heads: Optional[Iterable[int]] = None,
+                     rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """O [H, N, d] float64 for the keep mask (unlisted heads/rows stay zero)."""
+    H, N, d = q.shape
+    Hkv = k.shape[0]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    nb = N // block
+    out = np.zeros((H, N, d))
+    for h in (range(H) if heads is None else heads):
+        kv = kv_head_of(h, H, Hkv)
+        for I in (range(nb) if rows is None else rows):
+            blocks = np.nonzero(keep[h, I, : I + 1])[0]
+            out[h, I * block:(I + 1) * block] = sparse_attention_row(
+                q[h], k[kv], v[kv], blocks, I, block, scale)
+    return out
+
+
+def causal_keep(H: int, nb: int) -> np.ndarray:
+    """The full causal block mask (every J <= I kept): dense causal attention."""
+    return np.broadcast_to(np.tril(np.ones((nb, nb), dtype=bool)), (H, nb, nb)).copy()
+
+
+# --------------------------------------------------------------------------
+# whole pipeline
+# --------------------------------------------------------------------------
+def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
+             block: int = 128, scale: Optional[float] = None,
+             proxies_bf16: bool = True, with_output: bool = True) -> Dict[str, np.ndarray]:
+    """Run every step in order and return all intermediates."""
+    H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    qbar, kbar = proxy_pool(q, k, G, to_bf16=proxies_bf16)
+    S = proxy_scores(qbar, kbar, block, scale)
+    kh, masses = budgets(q, k, S, G, gamma, block, scale)
+    keep = select_blocks(S, kh, H)
+    res = {"qbar": qbar, "kbar": kbar, "S": S, "k_h": kh, "masses": masses, "keep": keep}
+    if with_output:
+        res["o"] = sparse_attention(q, k, v, keep, block, scale)
+    return res
+
+
+def kept_density(keep: np.ndarray) -> float:
+    """Kept fraction of causal blocks, a diagonal block counting one half."""
+    H, nb, _ = keep.shape
+    diag = np.trace(keep, axis1=1, axis2=2).sum()
+    return float((keep.sum() - 0.5 * diag) / (H * nb * nb / 2.0))

@@ -1,0 +1,321 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test compares an oracle function with brute force written differently
+(pure-Python loops, math.fsum), a library routine (torch CPU float64 scaled
+dot-product attention, torch's bfloat16 cast), a closed form or an invariant.
+Sizes are tiny so the whole module runs in seconds.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import proxyattn as O
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _brute_logit(qv, kv, scale):
+    return scale * math.fsum(float(a) * float(b) for a, b in zip(qv, kv))
+
+
+def _brute_block_scores(qp, kp, block, scale):
+    """Loops over every causal token pair and keeps the max per block pair."""
+    N = qp.shape[0]
+    nb = N // block
+    S = [[-math.inf] * nb for _ in range(nb)]
+    for i in range(N):
+        for j in range(i + 1):
+            s = _brute_logit(qp[i], kp[j], scale)
+            I, J = i // block, j // block
+            if s > S[I][J]:
+                S[I][J] = s
+    return np.array(S)
+
+
+# ---------------------------------------------------------------- rounding
+def test_round_bf16_matches_torch_cast():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e3).astype(np.float32),
+        # exact ties between two bfloat16 neighbours (round-half-even cases)
+        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.0 + 2.0 ** -7,
+                  0.0, -0.0, 1.0, -2.5], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------- pooling
+def test_pool_matches_loop_mean_and_group_map():
+    H, Hkv, N, d = 8, 4, 8, 3
+    q, k = _rand((H, N, d), 1), _rand((Hkv, N, d), 2)
+    for G in (1, 2, 4, 8):
+        qb, kb = O.proxy_pool(q, k, G, to_bf16=False)
+        for g in range(G):
+            qh = [h for h in range(H) if h * G // H == g]
+            kvs = sorted({h // (H // Hkv) for h in qh})
+            for t in range(N):
+                for e in range(d):
+                    assert qb[g, t, e] == pytest.approx(math.fsum(q[h, t, e] for h in qh) / len(qh), abs=1e-14)
+                    assert kb[g, t, e] == pytest.approx(math.fsum(k[c, t, e] for c in kvs) / len(kvs), abs=1e-14)
+
+
+def test_pool_identical_heads_and_permutation():
+    H, Hkv, N, d, G = 4, 2, 16, 4, 2
+    base = _rand((N, d), 3)
+    q = np.stack([base] * H)
+    k = np.stack([base * 2] * Hkv)
+    qb, kb = O.proxy_pool(q, k, G, to_bf16=False)
+    np.testing.assert_allclose(qb, np.stack([base] * G), atol=1e-15)
+    np.testing.assert_allclose(kb, np.stack([base * 2] * G), atol=1e-15)
+    q = _rand((H, N, d), 4)
+    perm = np.array([1, 0, 3, 2])  # swaps heads inside each group
+    a, _ = O.proxy_pool(q, k, G, to_bf16=False)
+    b, _ = O.proxy_pool(q[perm], k, G, to_bf16=False)
+    np.testing.assert_allclose(a, b, atol=1e-15)
+
+
+def test_pool_more_proxies_than_kv_heads_uses_the_one_kv_head():
+    H, Hkv, N, d, G = 8, 2, 4, 2, 4
+    q, k = _rand((H, N, d), 5), _rand((Hkv, N, d), 6)
+    _, kb = O.proxy_pool(q, k, G, to_bf16=False)
+    for g in range(G):
+        np.testing.assert_array_equal(kb[g], k[g // 2])
+
+
+# ---------------------------------------------------------------- scores (T1, T3, T5)
+@pytest.mark.parametrize("block,N,d", [(4, 12, 8), (3, 9, 5), (2, 8, 3)])
+def test_T1_scores_equal_bruteforce_maxpool(block, N, d):
+    G = 2
+    qp, kp = _rand((G, N, d), 7), _rand((G, N, d), 8)
+    scale = 0.37
+    S = O.proxy_scores(qp, kp, block, scale)
+    for g in range(G):
+        np.testing.assert_allclose(S[g], _brute_block_scores(qp[g], kp[g], block, scale), rtol=1e-12, atol=1e-12)
+
+
+def test_T1_scores_not_symmetric_in_q_k():
+    # A transposed operand (K.Q^T) would change the block scores of this case.
+    qp, kp = _rand((1, 8, 4), 9), _rand((1, 8, 4), 10) * 3
+    S = O.proxy_scores(qp, kp, 2, 1.0)
+    St = O.proxy_scores(kp, qp, 2, 1.0)
+    assert not np.allclose(S, St)
+    np.testing.assert_allclose(S[0], _brute_block_scores(qp[0], kp[0], 2, 1.0), rtol=1e-12)
+
+
+def test_T3_G_equals_H_reduces_to_per_head_scores():
+    H, Hkv, N, d, B = 4, 2, 12, 4, 4
+    q, k = _rand((H, N, d), 11), _rand((Hkv, N, d), 12)
+    qb, kb = O.proxy_pool(q, k, H, to_bf16=False)
+    S = O.proxy_scores(qb, kb, B, 0.5)
+    for h in range(H):
+        np.testing.assert_allclose(S[h], _brute_block_scores(q[h], k[h // 2], B, 0.5), rtol=1e-12)
+
+
+def test_T5_ranking_invariant_to_positive_rescale():
+    qp, kp = _rand((1, 32, 4), 13), _rand((1, 32, 4), 14)
+    S1 = O.proxy_scores(qp, kp, 4, 1.0)
+    for c in (2.0, 0.5, 3.7):
+        S2 = O.proxy_scores(qp * c, kp, 4, 1.0)
+        for I in range(8):
+            np.testing.assert_array_equal(O.rank_blocks(S1[0, I], I), O.rank_blocks(S2[0, I], I))
+
+
+def test_causal_mask_inside_diagonal_block():
+    # The only large logit sits above the diagonal (query 0, key 1); it must not count.
+    qp = np.zeros((1, 2, 1))
+    kp = np.zeros((1, 2, 1))
+    qp[0, 0, 0] = 1.0
+    kp[0, 1, 0] = 100.0
+    S = O.proxy_scores(qp, kp, 2, 1.0)
+    assert S[0, 0, 0] == 0.0
+
+
+# ---------------------------------------------------------------- ranking / selection (T9)
+def test_T9_selection_bruteforce_with_ties():
+    rng = np.random.default_rng(15)
+    nb = 12
+    for trial in range(50):
+        vals = rng.integers(0, 4, size=(nb, nb)).astype(np.float64)  # many ties
+        for I in range(nb):
+            order = O.rank_blocks(vals[I], I)
+            ref = sorted(range(I + 1), key=lambda J: (-vals[I, J], J))
+            assert list(order) == ref
+            for kk in range(1, nb + 2):
+                got = O.select_row(vals[I], I, kk)
+                want = sorted(set(ref[: min(kk, I + 1)]) | {I})
+                assert list(got) == want
+                assert I in got and np.all(np.diff(got) > 0) and got[-1] <= I
+                extra = 0 if I in ref[: min(kk, I + 1)] else 1
+                assert len(got) == min(kk, I + 1) + extra
+
+
+def test_T9_masks_nested_within_group():
+    H, G, nb = 4, 1, 10
+    S = np.tril(_rand((G, nb, nb), 16)) + np.triu(np.full((nb, nb), -np.inf), 1)
+    kh = [1, 3, 5, 10]
+    keep = O.select_blocks(S, kh, H)
+    for a, b in itertools.combinations(range(H), 2):
+        assert np.all(keep[a] <= keep[b])  # budgets ascending -> masks nested
+    assert np.all(np.diagonal(keep, axis1=1, axis2=2))
+    assert not np.any(np.triu(keep, 1))
+
+
+def test_ranking_uses_float32_stored_values():
+    # 1 + 1e-12 and 1 are the same float32 -> tie -> lower index first.
+    row = np.array([1.0, 1.0 + 1e-12])
+    assert list(O.rank_blocks(row, 1)) == [0, 1]
+
+
+# ---------------------------------------------------------------- budget (T7, T8)
+def _brute_masses(q_h, k_kv, block, scale):
+    N = q_h.shape[0]
+    nb = N // block
+    m = [0.0] * nb
+    for i in range(N - block, N):
+        logits = [_brute_logit(q_h[i], k_kv[j], scale) for j in range(i + 1)]
+        mx = max(logits)
+        w = [math.exp(x - mx) for x in logits]
+        z = math.fsum(w)
+        for j, wj in enumerate(w):
+            m[j // block] += wj / z / block
+    return np.array(m)
+
+
+def test_T7_masses_bruteforce_and_sum_to_one():
+    q, k = _rand((12, 4), 17, 2.0), _rand((12, 4), 18)
+    m = O.last_block_masses(q, k, 4, 0.6)
+    np.testing.assert_allclose(m, _brute_masses(q, k, 4, 0.6), rtol=1e-12, atol=1e-15)
+    assert m.sum() == pytest.approx(1.0, abs=1e-12)
+
+
+def test_T7_budget_is_minimal_prefix():
+    rng = np.random.default_rng(19)
+    for trial in range(300):
+        nb = int(rng.integers(1, 20))
+        m = rng.dirichlet(np.full(nb, 0.3))
+        order = rng.permutation(nb)
+        gamma = float(rng.uniform(0.01, 1.0))
+        kk = O.budget_from_masses(m, order, gamma)
+        prefix = lambda n: math.fsum(m[order[:n]])  # noqa: E731
+        if prefix(nb) >= gamma:
+            assert prefix(kk) >= gamma - 1e-12
+            assert kk == 1 or prefix(kk - 1) < gamma + 1e-12
+        else:
+            assert kk == nb
+
+
+def test_T8_budget_extremes():
+    m = np.array([0.1, 0.6, 0.3])
+    assert O.budget_from_masses(m, np.array([1, 2, 0]), 1e-9) == 1
+    assert O.budget_from_masses(m, np.array([1, 2, 0]), 1.0) in (2, 3)  # 0.6+0.3+0.1 == 1 up to rounding
+    assert O.budget_from_masses(np.array([0.5, 0.25]), np.array([0, 1]), 1.0) == 2  # never reached -> nb
+    assert O.budget_from_masses(m, np.array([0, 2, 1]), 0.4) == 2  # 0.1, 0.4 -> inclusive >=
+
+
+def test_budget_uses_last_row_ranking_of_own_group():
+    # Two groups whose last-row rankings differ; the masses favour block 0.
+    H, Hkv, G, B, N, d = 2, 2, 2, 2, 6, 2
+    q = np.zeros((H, N, d))
+    k = np.zeros((Hkv, N, d))
+    q[:, 4:, 0] = 5.0
+    k[:, 0:2, 0] = 1.0          # block 0 keys aligned with the last queries
+    S = np.full((G, 3, 3), -np.inf)
+    S[:, 0, 0] = 0
+    S[:, 1, :2] = 0
+    S[0, 2, :] = [3.0, 2.0, 1.0]   # group 0 ranks block 0 first
+    S[1, 2, :] = [1.0, 2.0, 3.0]   # group 1 ranks block 0 last
+    kh, m = O.budgets(q, k, S, G, 0.9, block=B, scale=1.0)
+    for h in range(H):
+        order = sorted(range(3), key=lambda J: -S[h, 2, J])
+        cum, want = 0.0, 3
+        for r, J in enumerate(order):
+            cum += m[h, J]
+            if cum >= 0.9:
+                want = r + 1
+                break
+        assert kh[h] == want
+    assert kh[0] == 1 and kh[1] == 3
+
+
+# ---------------------------------------------------------------- attention (T2, T4, T10, T11)
+def _sdpa64(q, k, v, scale, mask=None, causal=False):
+    H, Hkv = q.shape[0], k.shape[0]
+    kk = torch.from_numpy(np.repeat(k, H // Hkv, axis=0))
+    vv = torch.from_numpy(np.repeat(v, H // Hkv, axis=0))
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kk, vv, attn_mask=m, is_causal=causal, scale=scale).numpy()
+
+
+def test_T2_T4_full_mask_equals_library_causal_attention():
+    H, Hkv, N, d, B = 4, 2, 24, 8, 4
+    q, k, v = _rand((H, N, d), 20, 1.5), _rand((Hkv, N, d), 21), _rand((Hkv, N, d), 22)
+    out = O.sparse_attention(q, k, v, O.causal_keep(H, N // B), B, 0.4)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.4, causal=True), rtol=1e-12, atol=1e-12)
+
+
+def test_T2_gamma_one_pipeline_is_dense():
+    H, Hkv, N, d, B, G = 4, 2, 16, 4, 4, 2
+    q, k, v = _rand((H, N, d), 23, 0.5), _rand((Hkv, N, d), 24), _rand((Hkv, N, d), 25)
+    r = O.pipeline(q, k, v, G, 1.0, block=B)
+    assert r["keep"].sum() == H * (N // B) * (N // B + 1) // 2
+    np.testing.assert_allclose(r["o"], _sdpa64(q, k, v, 1 / math.sqrt(d), causal=True), rtol=1e-12, atol=1e-12)
+
+
+def test_T10_diagonal_only_is_blockwise_local_attention():
+    H, Hkv, N, d, B = 2, 1, 16, 4, 4
+    q, k, v = _rand((H, N, d), 26), _rand((Hkv, N, d), 27), _rand((Hkv, N, d), 28)
+    keep = np.zeros((H, N // B, N // B), dtype=bool)
+    for I in range(N // B):
+        keep[:, I, I] = True
+    out = O.sparse_attention(q, k, v, keep, B, 0.5)
+    for I in range(N // B):
+        s = slice(I * B, (I + 1) * B)
+        ref = _sdpa64(q[:, s].copy(), k[:, s].copy(), v[:, s].copy(), 0.5, causal=True)
+        np.testing.assert_allclose(out[:, s], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_T11_any_mask_equals_dense_with_minus_inf_bias():
+    H, Hkv, N, d, B = 2, 1, 20, 4, 4
+    nb = N // B
+    rng = np.random.default_rng(29)
+    q, k, v = _rand((H, N, d), 30), _rand((Hkv, N, d), 31), _rand((Hkv, N, d), 32)
+    keep = np.tril(rng.random((H, nb, nb)) < 0.5)
+    for I in range(nb):
+        keep[:, I, I] = True
+    tok = np.repeat(np.repeat(keep, B, axis=1), B, axis=2) & np.tril(np.ones((N, N), dtype=bool))
+    out = O.sparse_attention(q, k, v, keep, B, 0.5)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.5, mask=tok), rtol=1e-12, atol=1e-12)
+
+
+def test_kept_density_counts_diagonal_half():
+    keep = O.causal_keep(3, 5)
+    assert O.kept_density(keep) == pytest.approx(1.0)
+    diag = np.zeros((3, 5, 5), dtype=bool)
+    for I in range(5):
+        diag[:, I, I] = True
+    assert O.kept_density(diag) == pytest.approx(0.5 * 5 / (25 / 2))
+
+
+def test_heads_use_their_own_groups_scores():
+    # H=4, G=2: heads 0,1 form group 0 and heads 2,3 group 1 (consecutive runs).
+    H, G, nb = 4, 2, 6
+    rng = np.random.default_rng(33)
+    S = np.full((G, nb, nb), -np.inf)
+    for g in range(G):
+        for I in range(nb):
+            S[g, I, : I + 1] = rng.permutation(I + 1).astype(float)
+    kh = [2, 2, 2, 2]
+    keep = O.select_blocks(S, kh, H)
+    for h, g in zip(range(H), [0, 0, 1, 1]):
+        for I in range(nb):
+            ref = sorted(range(I + 1), key=lambda J: (-S[g, I, J], J))[: min(2, I + 1)]
+            assert list(np.nonzero(keep[h, I])[0]) == sorted(set(ref) | {I})
+    assert [O.group_of(h, H, G) for h in range(H)] == [0, 0, 1, 1]
