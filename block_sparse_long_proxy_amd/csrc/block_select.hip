@@ -1,0 +1,164 @@
+// block_select.hip -- block ranking + per-head top-k -> CSR block mask.
+//
+// ProxyAttn blog post (ir.hit.edu.cn), section 4, step 1 "Block Ranking": the
+// key blocks of each row are ranked by the proxy block scores and the top
+// blocks within a budget are kept; the final step combines that ranking with
+// the per-head budgets of step 2 into the block sparse mask.  Row (h, I)
+// keeps the first min(k_h, I+1) blocks of its group's ranking (score
+// descending, block ascending on ties) plus the diagonal block I.
+//
+// Three launches:
+//   select_count_kernel: one wave per (g, I); the rank of the diagonal block
+//     is a plain count of blocks ahead of it, so the row lengths (and hence
+//     row_ptr) are known without sorting.
+//   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr.
+//   select_emit_kernel : one workgroup per (g, I); bitonic sort of the row's
+//     64-bit (score, index) keys in LDS gives every block's rank; each head
+//     of the group then compacts {J : rank < k or J == I} in ascending J.
+#include "pxa_device.hpp"
+#include "pxa_launch.hpp"
+
+namespace pxa {
+
+constexpr int kEmitThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(256) void select_count_kernel(const float* __restrict__ scores,
+                                                           const int32_t* __restrict__ k_h,
+                                                           int32_t* __restrict__ counts, int H,
+                                                           int G, int nb) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // g * nb + I
+  const int l = threadIdx.x & 63;
+  if (row >= G * nb) return;
+  const int g = row / nb, I = row % nb;
+  const float* s = scores + (size_t)row * nb;
+  const uint64_t kd = rank_key(s[I], (uint32_t)I);
+  int ahead = 0;
+  for (int J = l; J < I; J += 64) ahead += rank_key(s[J], (uint32_t)J) < kd ? 1 : 0;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ahead += __shfl_xor(ahead, o, 64);
+  const int hpg = H / G;
+  for (int hh = l; hh < hpg; hh += 64) {
+    const int h = g * hpg + hh;
+    const int kk = max(0, min(k_h[h], I + 1));   // negative budgets: diagonal only
+    counts[(size_t)h * nb + I] = kk + (ahead >= kk ? 1 : 0);
+  }
+}
+
+// Exclusive scan of n counts into row_ptr[0..n]; one workgroup.
+__global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ row_ptr,
+                                                                   int n) {
+  __shared__ int part[kScanThreads];
+  const int t = threadIdx.x;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int a = min(n, t * per), b = min(n, a + per);
+  int s = 0;
+  for (int i = a; i < b; ++i) s += counts[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele
+    const int x = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+  int run = part[t] - s;
+  for (int i = a; i < b; ++i) {
+    row_ptr[i] = run;
+    run += counts[i];
+  }
+  if (t == kScanThreads - 1) row_ptr[n] = part[t];
+}
+
+__global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
+    const float* __restrict__ scores, const int32_t* __restrict__ k_h,
+    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int H, int G, int nb,
+    int Pmax) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);          // [Pmax]
+  uint16_t* rank = reinterpret_cast<uint16_t*>(keys + Pmax);   // [nb]
+  __shared__ int wsum[kEmitThreads / 64];
+
+  // Heavy rows first: blockIdx.x -> (I descending, g).
+  const int I = nb - 1 - (int)(blockIdx.x / G);
+  const int g = (int)(blockIdx.x % G);
+  const int n = I + 1;
+  int P = 1;
+  while (P < n) P <<= 1;
+  const int t = threadIdx.x;
+  const float* s = scores + ((size_t)g * nb + I) * nb;
+  for (int J = t; J < P; J += kEmitThreads)
+    keys[J] = J < n ? rank_key(s[J], (uint32_t)J) : ~0ull;
+  __syncthreads();
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < P / 2; i += kEmitThreads) {
+        const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int b = a + j;
+        const uint64_t x = keys[a], y = keys[b];
+        const bool up = (a & kk) == 0;
+        if ((x > y) == up) {
+          keys[a] = y;
+          keys[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = t; r < n; r += kEmitThreads) rank[(uint32_t)keys[r]] = (uint16_t)r;
+  __syncthreads();
+
+  // Contiguous chunk of J per thread so the output stays in ascending order.
+  const int per = (n + kEmitThreads - 1) / kEmitThreads;
+  const int a0 = min(n, t * per), a1 = min(n, a0 + per);
+  const int hpg = H / G;
+  const int wv = t >> 6, ln = t & 63;
+  for (int hh = 0; hh < hpg; ++hh) {
+    const int h = g * hpg + hh;
+    const int kk = max(0, min(k_h[h], n));
+    int c = 0;
+    for (int J = a0; J < a1; ++J) c += (rank[J] < kk || J == I) ? 1 : 0;
+    // exclusive scan of c over the workgroup
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (ln >= o) incl += y;
+    }
+    if (ln == 63) wsum[wv] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wv; ++i) base += wsum[i];
+    int pos = row_ptr[(size_t)h * nb + I] + base + incl - c;
+    for (int J = a0; J < a1; ++J)
+      if (rank[J] < kk || J == I) col_idx[pos++] = J;
+    __syncthreads();   // wsum reused by the next head
+  }
+}
+
+size_t select_ws_bytes(const LaunchArgs& a) {
+  return align_up((size_t)a.H * (a.N / kBlock) * sizeof(int32_t), 256);
+}
+
+hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
+                         int32_t* row_ptr, int32_t* col_idx, void* ws, hipStream_t stream) {
+  const int nb = a.N / kBlock;
+  int32_t* counts = (int32_t*)ws;
+  hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,
+                     k_h, counts, a.H, a.G, nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr,
+                     a.H * nb);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int Pmax = 1;
+  while (Pmax < nb) Pmax <<= 1;
+  const size_t smem = (size_t)Pmax * 8 + align_up((size_t)nb * 2, 16);
+  hipLaunchKernelGGL(select_emit_kernel, dim3(a.G * nb), dim3(kEmitThreads), smem, stream, scores,
+                     k_h, row_ptr, col_idx, a.H, a.G, nb, Pmax);
+  return hipGetLastError();
+}
+
+}  // namespace pxa

@@ -1,0 +1,155 @@
+// fa_prefill.hip -- block-sparse (and dense) causal prefill attention.
+//
+// ProxyAttn blog post (ir.hit.edu.cn), section 4, final step: the block
+// sparse mask goes to FlashAttention; section 2: a kept block is a whole
+// 128x128 tile so the tiled kernel can skip the rest.  O = softmax(scale QK^T)V
+// restricted to kept blocks and j <= i, online softmax in fp32.
+//
+// One workgroup = one (head h, query block I); 4 waves x 32 queries.  For
+// every kept key block J (diagonal first, then descending J) the K tile and
+// the transposed V tile are staged through LDS and the wave computes
+//   S^T = K Q^T (32 MFMA 32x32x16), online softmax in registers,
+//   O^T += V^T P^T (32 MFMA).
+#include "pxa_device.hpp"
+#include "pxa_launch.hpp"
+
+namespace pxa {
+
+template <int D, bool DENSE>
+__global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
+    __bf16* __restrict__ o, int H, int Hkv, int N, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
+  __shared__ __attribute__((aligned(16))) __bf16 vts[D * kBlock];
+
+  const int nb = N / kBlock;
+  // Heavy rows first: blockIdx.x -> (I descending, h).
+  const int I = nb - 1 - (int)(blockIdx.x / H);
+  const int h = (int)(blockIdx.x % H);
+  const int kvh = h / (H / Hkv);
+  const int w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int qloc = 32 * w + (l & 31);          // query index inside block I
+
+  const __bf16* kbase = k + (size_t)kvh * N * D;
+  const __bf16* vbase = v + (size_t)kvh * N * D;
+
+  bf16x8 qf[D / 16];
+  load_qfrag<D>(q + ((size_t)h * N + (size_t)I * kBlock + qloc) * D, qf);
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) oacc[m] = zero16();
+  float m_run = -INFINITY;   // running max of raw logits (this lane's query)
+  float l_run = 0.f;         // this lane's partial row sum (its 64 keys / block)
+
+  int beg, end;
+  if (DENSE) {
+    beg = 0;
+    end = I + 1;
+  } else {
+    beg = row_ptr[h * nb + I];
+    end = row_ptr[h * nb + I + 1];
+  }
+
+  for (int it = end - 1; it >= beg; --it) {
+    const int J = DENSE ? it : col_idx[it];
+    if (J < 0 || J > I) continue;               // uniform across the workgroup
+    __syncthreads();                              // previous tile fully consumed
+    stage_ktile<D>(kbase + (size_t)J * kBlock * D, ks);
+    stage_vtile<D>(vbase + (size_t)J * kBlock * D, vts);
+    __syncthreads();
+
+    f32x16 s[4];
+    tile_scores<D>(ks, qf, s);
+
+    if (J == I) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (acc_key(t, r) > qloc) s[t][r] = -INFINITY;
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    // m_new is finite once any unmasked key has been seen (always true after
+    // the diagonal block, which comes first when present).
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f((m_run - m_use) * scale_log2);
+    m_run = m_new;
+    const float mb = m_use * scale_log2;
+
+    bf16x8 pb[4][2];
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(fmaf(s[t][r], scale_log2, -mb));
+        lsum += p;
+        pb[t][r >> 3][r & 7] = (__bf16)p;
+      }
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m)
+          oacc[m] = mfma32(vtile_frag(vts, m, t, s2), pb[t][s2], oacc[m]);
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  __bf16* orow = o + ((size_t)h * N + (size_t)I * kBlock + qloc) * D;
+  const int hi = l >> 5;
+#pragma unroll
+  for (int m = 0; m < D / 32; ++m) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 ov;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(oacc[m][4 * g4 + e] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 32 * m + 8 * g4 + 4 * hi) = ov;
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, const void* v,
+                            const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
+                            hipStream_t stream) {
+  const dim3 grid(a.H * (a.N / kBlock)), block(kThreads);
+  const float sl2 = a.scale * kLog2e;
+  if (dense)
+    hipLaunchKernelGGL((fa_prefill_kernel<D, true>), grid, block, 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                       (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+  else
+    hipLaunchKernelGGL((fa_prefill_kernel<D, false>), grid, block, 0, stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
+                       (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+  return hipGetLastError();
+}
+
+hipError_t launch_fa_prefill(const LaunchArgs& a, const void* q, const void* k, const void* v,
+                             const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
+                             hipStream_t stream) {
+  return a.D == 64 ? launch_fa<64>(a, q, k, v, row_ptr, col_idx, o, dense, stream)
+                   : launch_fa<128>(a, q, k, v, row_ptr, col_idx, o, dense, stream);
+}
+
+}  // namespace pxa

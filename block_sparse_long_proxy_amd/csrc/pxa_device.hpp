@@ -1,0 +1,203 @@
+// pxa_device.hpp -- device building blocks shared by the gfx950 kernels.
+//
+// MFMA operand layouts used throughout (v_mfma_f32_32x32x16_bf16, wave64,
+// lane l, hi = l / 32):
+//   A (32 x 16, M x K): lane holds A[l % 32][8*hi .. 8*hi+7]
+//   B (16 x 32, K x N): lane holds B[8*hi .. 8*hi+7][l % 32]
+//   C (32 x 32)       : register r holds C[8*(r/4) + 4*hi + r%4][l % 32]
+//
+// Attention tiles are computed transposed: S^T = K . Q^T, so a lane owns one
+// query column (n = l % 32) and 16 key rows per 32-key sub-tile.  Row-wise
+// softmax statistics are then mostly in-lane, and the probabilities already
+// sit in the B-operand layout of O^T += V^T . P^T (the key index is the
+// contraction index, in the permuted order the C layout gives).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pxa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 128;     // key/query block edge (tokens)
+constexpr int kWaves = 4;       // waves per workgroup in the tile kernels
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Row-major [128][D] bf16 tile in LDS with a 16-byte-chunk XOR swizzle:
+// chunk c of row r lives at chunk (c ^ (r & (D/8 - 1))).  A wave reading one
+// chunk column from 32 consecutive rows touches every bank group once.
+template <int D>
+__device__ __forceinline__ int ktile_off(int row, int chunk) {
+  constexpr int C = D / 8;
+  return row * D + ((chunk ^ (row & (C - 1))) << 3);
+}
+
+// Copy a [128][D] bf16 tile (rows `row_stride` elements apart in global
+// memory) into the swizzled LDS layout.  All kThreads threads participate.
+template <int D>
+__device__ __forceinline__ void stage_ktile(const __bf16* __restrict__ g, __bf16* lds) {
+  constexpr int C = D / 8;                 // 16-byte chunks per row
+  constexpr int ITER = kBlock * C / kThreads;
+  const int t = threadIdx.x;
+  u32x4 buf[ITER];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int c = it * kThreads + t;
+    const int r = c / C, cc = c % C;
+    buf[it] = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + cc * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int c = it * kThreads + t;
+    const int r = c / C, cc = c % C;
+    *reinterpret_cast<u32x4*>(lds + ktile_off<D>(r, cc)) = buf[it];
+  }
+}
+
+// A operand (keys x d) of sub-tile `t` (32 keys) and k-step `s` (16 dims).
+template <int D>
+__device__ __forceinline__ bf16x8 ktile_frag(const __bf16* lds, int t, int s) {
+  const int l = threadIdx.x & 63;
+  const int row = t * 32 + (l & 31);
+  const int chunk = 2 * s + (l >> 5);
+  return *reinterpret_cast<const bf16x8*>(lds + ktile_off<D>(row, chunk));
+}
+
+// B operand (d x queries) for k-step s, read straight from global memory:
+// query row `qrow` (pointer to its first element), dims 16 s + 8 hi .. +7.
+template <int D>
+__device__ __forceinline__ void load_qfrag(const __bf16* __restrict__ qrow, bf16x8 (&qf)[D / 16]) {
+  const int hi = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi);
+}
+
+// S^T (128 keys x 32 queries of this wave) = K_tile . Q^T, four 32x32 tiles.
+template <int D>
+__device__ __forceinline__ void tile_scores(const __bf16* ks, const bf16x8 (&qf)[D / 16], f32x16 (&acc)[4]) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = zero16();
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = mfma32(ktile_frag<D>(ks, t, s), qf[s], acc[t]);
+  }
+}
+
+// Key index (0..127 inside the block) held by register r of sub-tile t.
+__device__ __forceinline__ int acc_key(int t, int r) {
+  const int hi = (threadIdx.x & 63) >> 5;
+  return t * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
+// V^T tile in LDS: [D][128] bf16 (keys contiguous per dim row), stored in
+// 8-byte chunks (4 keys) with chunk c of row d at chunk (c ^ (d & 31)).
+__device__ __forceinline__ int vt_off(int d, int chunk8) {
+  return d * kBlock + ((chunk8 ^ (d & 31)) << 2);
+}
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi16, b.hi16)
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Copy a [128 keys][D] bf16 V tile into the transposed LDS layout.  Each
+// participating thread moves one 8x8 (keys x dims) sub-block and transposes
+// it in registers.
+template <int D>
+__device__ __forceinline__ void stage_vtile(const __bf16* __restrict__ g, __bf16* lds) {
+  constexpr int C = D / 8;
+  constexpr int SUB = (kBlock / 8) * C;   // 8x8 sub-blocks per tile
+  const int t = threadIdx.x;
+  for (int sb = t; sb < SUB; sb += kThreads) {
+    const int a = sb / C, b = sb % C;     // key group, dim group
+    u32x4 in[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      in[kk] = *reinterpret_cast<const u32x4*>(g + (size_t)(8 * a + kk) * D + 8 * b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // out row: dim 8b+e, keys 8a..8a+7 -> 4 u32 words of 2 keys each
+      u32x2 w0, w1;
+      const int word = e >> 1;
+      if (e & 1) {
+        w0[0] = pack_hi(in[0][word], in[1][word]);
+        w0[1] = pack_hi(in[2][word], in[3][word]);
+        w1[0] = pack_hi(in[4][word], in[5][word]);
+        w1[1] = pack_hi(in[6][word], in[7][word]);
+      } else {
+        w0[0] = pack_lo(in[0][word], in[1][word]);
+        w0[1] = pack_lo(in[2][word], in[3][word]);
+        w1[0] = pack_lo(in[4][word], in[5][word]);
+        w1[1] = pack_lo(in[6][word], in[7][word]);
+      }
+      const int d = 8 * b + e;
+      *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a)) = w0;
+      *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a + 1)) = w1;
+    }
+  }
+}
+
+// A operand of O^T += V^T . P^T: dims 32 m + l%32, the 8 keys that the C
+// layout of sub-tile t gives this lane for half `s2` (registers 8 s2 .. +7):
+// keys 32t + 16 s2 + 4 hi + {0..3} and the same + 8.
+__device__ __forceinline__ bf16x8 vtile_frag(const __bf16* lds, int m, int t, int s2) {
+  const int l = threadIdx.x & 63;
+  const int hi = l >> 5;
+  const int d = 32 * m + (l & 31);
+  const int c0 = (32 * t + 16 * s2 + 4 * hi) >> 2;
+  u32x2 x = *reinterpret_cast<const u32x2*>(lds + vt_off(d, c0));
+  u32x2 y = *reinterpret_cast<const u32x2*>(lds + vt_off(d, c0 + 2));
+  u32x4 v;
+  v[0] = x[0]; v[1] = x[1]; v[2] = y[0]; v[3] = y[1];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Order-preserving map of a finite float to uint32 (larger float -> larger
+// code); -0 is folded onto +0 first so that equal scores compare equal.
+__device__ __forceinline__ uint32_t float_order_key(float f) {
+  f = f + 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Sort key of block J with score s: ascending key order == score descending,
+// then block index ascending.
+__device__ __forceinline__ uint64_t rank_key(float s, uint32_t J) {
+  return ((uint64_t)(~float_order_key(s)) << 32) | (uint64_t)J;
+}
+
+}  // namespace pxa

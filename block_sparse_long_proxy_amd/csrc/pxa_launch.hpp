@@ -1,0 +1,36 @@
+// pxa_launch.hpp -- host-side launch interface between the C ABI layer and
+// the kernel files.  Arguments are validated by the ABI layer before any of
+// these is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pxa {
+
+constexpr int kBlockTokens = 128;   // block edge the kernels are built for
+
+struct LaunchArgs {
+  int H, Hkv, N, D, G;
+  float scale;   // softmax scale (already defaulted)
+  float gamma;
+};
+
+hipError_t launch_proxy_pool(const LaunchArgs& a, const void* q, const void* k, void* qbar,
+                             void* kbar, hipStream_t stream);
+hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,
+                              float* scores, hipStream_t stream);
+// ws: budget_ws_bytes(a) bytes
+size_t budget_ws_bytes(const LaunchArgs& a);
+hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, const float* scores,
+                         int32_t* k_h, float* masses, void* ws, hipStream_t stream);
+// ws: select_ws_bytes(a) bytes
+size_t select_ws_bytes(const LaunchArgs& a);
+hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
+                         int32_t* row_ptr, int32_t* col_idx, void* ws, hipStream_t stream);
+hipError_t launch_fa_prefill(const LaunchArgs& a, const void* q, const void* k, const void* v,
+                             const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
+                             hipStream_t stream);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace pxa

@@ -1,0 +1,166 @@
+/*
+ * pxa.h -- C ABI of the MI355X (gfx950) ProxyAttn block-sparse causal prefill
+ * attention library (libpxa.so).
+ *
+ * Method: "ProxyAttn" as described in the ProxyAttn blog post
+ * (ir.hit.edu.cn, "ProxyAttn ... ICLR 2026"), section 4 ("ProxyAttn方法详解"):
+ *   step 1: pool Q and K over the heads of a group into proxy heads, estimate
+ *           token-level proxy scores and max-pool them to 128x128 block scores,
+ *           rank the key blocks of each query-block row;
+ *   step 2: estimate each head's block budget from the last query block;
+ *   final:  turn ranking + budgets into a block-sparse mask and run
+ *           FlashAttention-style attention over the kept blocks only.
+ * The abstract on the arXiv listing page (mlsanity.com, "ProxyAttn: Guided
+ * Sparse Attention via Representative Heads") names the same parts:
+ * representative (pooled) heads and block-aware dynamic budget estimation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Batch 1, causal prefill.  H query heads, Hkv KV heads, N tokens, head
+ *    dimension d, block B = 128, nb = N / B key/query blocks, G proxies.
+ *  - Query head h uses KV head h / (H / Hkv).  Proxy group g holds query heads
+ *    [g*H/G, (g+1)*H/G) and the (contiguous) KV heads those use.
+ *  - Q, O: bfloat16 [H][N][d]; K, V: bfloat16 [Hkv][N][d]; proxies Qbar, Kbar:
+ *    bfloat16 [G][N][d]; all row-major and contiguous.  Tensor pointers are
+ *    device pointers, 16-byte aligned; int32/fp32 arrays 4-byte aligned;
+ *    workspaces 256-byte aligned.
+ *  - The caller owns every buffer (inputs, outputs, workspace).  The library
+ *    never allocates, frees or synchronises; it enqueues kernels on `stream`
+ *    (a hipStream_t; NULL = the null stream) and returns.  Buffers must stay
+ *    valid until that stream work completes.  No global mutable state: calls
+ *    on different streams with different buffers may run concurrently.
+ *  - Return value: PXA_OK (0) or a negative PXA_E* code.  Every argument is
+ *    validated on the host before anything is launched, so an error return
+ *    means nothing was enqueued, except PXA_EHIP (a launch failed; earlier
+ *    kernels of the same call may have been enqueued).  Inputs are assumed
+ *    finite (NaN/Inf are not checked).  Results are deterministic for a given
+ *    device and inputs.
+ */
+#ifndef PXA_H
+#define PXA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PXA_ABI_VERSION 1
+
+enum {
+  PXA_OK = 0,
+  PXA_EINVAL = -1,       /* inconsistent shape, grouping, gamma or scale     */
+  PXA_EUNSUPPORTED = -2, /* d not 64/128, block not 128, N % 128 != 0, N too big */
+  PXA_ENULL = -3,        /* a required pointer is NULL                       */
+  PXA_EALIGN = -4,       /* a pointer violates its alignment requirement    */
+  PXA_EWORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes query */
+  PXA_EHIP = -6          /* a kernel launch failed (see pxa_last_hip_error)  */
+};
+
+/* Problem description.  Plain data; the library keeps no pointer to it. */
+typedef struct pxa_config {
+  int32_t num_heads;     /* H  >= 1                                              */
+  int32_t num_kv_heads;  /* Hkv >= 1, H % Hkv == 0                               */
+  int32_t seq_len;       /* N, a multiple of 128, 128 <= N <= 524288             */
+  int32_t head_dim;      /* d, 64 or 128                                         */
+  int32_t block;         /* must be 128 (blog post section 2: 128x128 blocks)    */
+  int32_t num_proxies;   /* G: H % G == 0 and (Hkv % G == 0 or G % Hkv == 0)     */
+  float gamma;           /* budget threshold, 0 < gamma <= 1                     */
+  float softmax_scale;   /* > 0, or <= 0 for 1/sqrt(d)                           */
+} pxa_config;
+
+/* Sizes and offsets of the whole-pipeline workspace (bytes from its start).
+ * Intermediates are left there by pxa_prefill so a caller can inspect them. */
+typedef struct pxa_workspace_layout {
+  size_t qbar;      /* bf16 [G][N][d]                    */
+  size_t kbar;      /* bf16 [G][N][d]                    */
+  size_t scores;    /* fp32 [G][nb][nb]                  */
+  size_t masses;    /* fp32 [H][nb]                      */
+  size_t k_h;       /* int32 [H]                         */
+  size_t row_ptr;   /* int32 [H*nb + 1]                  */
+  size_t col_idx;   /* int32 [H*nb*(nb+1)/2] (capacity)  */
+  size_t budget_ws; /* pxa_budget_workspace_bytes        */
+  size_t select_ws; /* pxa_select_workspace_bytes        */
+  size_t total;     /* == pxa_workspace_bytes            */
+} pxa_workspace_layout;
+
+/* ---- queries (host only, no device work) ------------------------------- */
+int pxa_abi_version(void);
+const char* pxa_strerror(int code);
+/* Message of the last HIP error seen by a PXA_EHIP return on this thread. */
+const char* pxa_last_hip_error(void);
+/* PXA_OK if the configuration is valid, else the code a call would return. */
+int pxa_validate_config(const pxa_config* cfg);
+/* Whole-pipeline workspace size in bytes; 0 if cfg is invalid. */
+size_t pxa_workspace_bytes(const pxa_config* cfg);
+int pxa_get_workspace_layout(const pxa_config* cfg, pxa_workspace_layout* out);
+/* Scratch needed by pxa_budget_estimate / pxa_block_select; 0 if invalid. */
+size_t pxa_budget_workspace_bytes(const pxa_config* cfg);
+size_t pxa_select_workspace_bytes(const pxa_config* cfg);
+/* Capacity col_idx must have: H * nb * (nb + 1) / 2 entries (every causal block). */
+size_t pxa_max_col_entries(const pxa_config* cfg);
+
+/* ---- the pipeline ------------------------------------------------------- */
+
+/* Whole method on one layer: proxy pool -> proxy scores -> budgets -> block
+ * selection -> block-sparse attention.  q/k/v inputs, o output (layouts
+ * above); ws of at least pxa_workspace_bytes(cfg) bytes, laid out as
+ * pxa_get_workspace_layout reports. */
+int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
+                void* o, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 1, head pooling (blog post section 4, step 1 "Head Pooling"; section 3
+ * calls it a simple pooling).  qbar[g] = mean of q over the group's query
+ * heads, kbar[g] = mean of k over the group's KV heads; fp32 sums, one
+ * round-to-nearest-even conversion to bf16 per element. */
+int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k,
+                   void* qbar, void* kbar, void* stream);
+
+/* Step 1, score estimation (section 4, step 1 "Score Estimation": token-level
+ * proxy scores, block max-pool, the QK product fused with the pooling).
+ * scores[g][I][J] = scale * max over causal token pairs (i in block I,
+ * j in block J, j <= i) of qbar[g][i] . kbar[g][j], fp32, for J <= I; -inf
+ * for J > I.  bf16 MFMA products, fp32 accumulation. */
+int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar,
+                    float* scores, void* stream);
+
+/* Step 2, dynamic budget (section 4, step 2: the last query block estimates
+ * each head's block-level sparsity; the abstract's "block-aware dynamic budget
+ * estimation").  For head h: masses[h][J] = mean over the last B queries of
+ * their exact causal softmax mass in key block J (fp32); k_h[h] = smallest k
+ * such that the masses of the first k blocks of the group's ranking of row
+ * nb-1 (score descending, block ascending on ties) sum to >= gamma, else nb.
+ * scores: as written by pxa_proxy_score.  ws: pxa_budget_workspace_bytes. */
+int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k,
+                        const float* scores, int32_t* k_h, float* masses,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Step 1 ranking + final mask (section 4, step 1 "Block Ranking" with TopK,
+ * and the final block sparse mask handed to FlashAttention).  Row (h, I)
+ * keeps the first min(k_h[h], I+1) blocks of the group's ranking of row I
+ * plus the diagonal block I.  Output is CSR over rows r = h*nb + I:
+ * row_ptr[H*nb+1], col_idx[row_ptr[r] .. row_ptr[r+1]) ascending.
+ * col_idx needs pxa_max_col_entries(cfg) capacity; ws: pxa_select_workspace_bytes. */
+int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
+                     int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* Block-sparse causal attention over the CSR mask (section 4, final step; the
+ * attention of section 2).  o[h][i] = sum of softmax(scale * q.k_j) v_j over
+ * the keys j <= i of the kept blocks of row (h, i / B), renormalised over
+ * them; fp32 online softmax, bf16 MFMA products, bf16 output (RNE).  Entries
+ * of a row outside [0, I] are ignored; a row with no valid entry yields zeros. */
+int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
+                       const int32_t* row_ptr, const int32_t* col_idx, void* o,
+                       void* stream);
+
+/* Dense causal attention with the same kernel (every block J <= I kept):
+ * the baseline the sparse path is measured against. */
+int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
+                      void* o, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PXA_H */

@@ -1,0 +1,161 @@
+"""Host-only tests of the C ABI: symbols, validation and workspace sizing.
+
+No compute call reaches a launch here: every call either is a pure query or
+fails host-side validation (which runs before anything is enqueued), so these
+run without a GPU.  Addresses are fake integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_proxy_amd as pxa
+from block_sparse_long_proxy_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 1 << 20          # a 256-byte aligned fake address
+MIS = A + 2          # misaligned for 16-byte tensors
+
+
+def _good(**kw):
+    d = dict(num_heads=8, num_kv_heads=2, seq_len=1024, head_dim=128, num_proxies=2, gamma=0.9)
+    d.update(kw)
+    return pxa.Config(**d)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pxa.load_library()
+    with open(os.path.join(ROOT, "include", "pxa.h")) as f:
+        hdr = f.read()
+    names = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(pxa_\w+)\s*\(", hdr, re.M))
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B._SIGNATURES, n
+    assert pxa.pxa_abi_version() == 1
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(B.pxa_config) == 32
+    assert ctypes.sizeof(B.pxa_workspace_layout) == 10 * ctypes.sizeof(ctypes.c_size_t)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), B.PXA_OK),
+    (dict(num_heads=0), B.PXA_EINVAL),
+    (dict(num_kv_heads=3), B.PXA_EINVAL),            # 8 % 3
+    (dict(num_kv_heads=16), B.PXA_EINVAL),           # more KV than query heads
+    (dict(num_proxies=3), B.PXA_EINVAL),             # 8 % 3
+    (dict(num_heads=12, num_kv_heads=4, num_proxies=6), B.PXA_EINVAL),  # 4 % 6, 6 % 4
+    (dict(num_proxies=8), B.PXA_OK),                 # G % Hkv == 0
+    (dict(num_proxies=1), B.PXA_OK),
+    (dict(gamma=0.0), B.PXA_EINVAL),
+    (dict(gamma=1.0), B.PXA_OK),
+    (dict(gamma=1.01), B.PXA_EINVAL),
+    (dict(gamma=float("nan")), B.PXA_EINVAL),
+    (dict(softmax_scale=float("inf")), B.PXA_EINVAL),
+    (dict(softmax_scale=-1.0), B.PXA_OK),            # default scale
+    (dict(head_dim=96), B.PXA_EUNSUPPORTED),
+    (dict(head_dim=64), B.PXA_OK),
+    (dict(block=64), B.PXA_EUNSUPPORTED),
+    (dict(seq_len=1000), B.PXA_EUNSUPPORTED),
+    (dict(seq_len=128), B.PXA_OK),
+    (dict(seq_len=1 << 20), B.PXA_EUNSUPPORTED),
+])
+def test_validate_config_codes(kw, code):
+    assert pxa.pxa_validate_config(_good(**kw)) == code
+
+
+def test_invalid_config_has_zero_sizes():
+    bad = _good(head_dim=96)
+    assert pxa.pxa_workspace_bytes(bad) == 0
+    assert pxa.pxa_budget_workspace_bytes(bad) == 0
+    assert pxa.pxa_select_workspace_bytes(bad) == 0
+    assert pxa.pxa_max_col_entries(bad) == 0
+    with pytest.raises(pxa.PxaError) as e:
+        pxa.pxa_get_workspace_layout(bad)
+    assert e.value.code == B.PXA_EUNSUPPORTED
+
+
+def test_workspace_layout_is_ordered_aligned_and_sized():
+    cfg = _good()
+    L = pxa.pxa_get_workspace_layout(cfg)
+    H, G, N, d, nb = 8, 2, 1024, 128, 8
+    parts = [("qbar", G * N * d * 2), ("kbar", G * N * d * 2), ("scores", G * nb * nb * 4),
+             ("masses", H * nb * 4), ("k_h", H * 4), ("row_ptr", (H * nb + 1) * 4),
+             ("col_idx", H * nb * (nb + 1) // 2 * 4),
+             ("budget_ws", pxa.pxa_budget_workspace_bytes(cfg)),
+             ("select_ws", pxa.pxa_select_workspace_bytes(cfg))]
+    prev_end = 0
+    for name, size in parts:
+        off = getattr(L, name)
+        assert off % 256 == 0 and off >= prev_end, name
+        prev_end = off + size
+    assert L.total >= prev_end and L.total == pxa.pxa_workspace_bytes(cfg)
+    assert pxa.pxa_max_col_entries(cfg) == H * nb * (nb + 1) // 2
+    assert pxa.pxa_budget_workspace_bytes(cfg) >= H * nb * 128 * 4
+    assert pxa.pxa_select_workspace_bytes(cfg) >= H * nb * 4
+
+
+def _expect(code, fn, *args, **kw):
+    with pytest.raises(pxa.PxaError) as e:
+        fn(*args, **kw)
+    assert e.value.code == code, e.value
+
+
+def test_compute_entry_points_reject_bad_config_before_launch():
+    bad = _good(num_heads=7)
+    _expect(B.PXA_EINVAL, pxa.pxa_proxy_pool, bad, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_proxy_score, bad, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_budget_estimate, bad, A, A, A, A, A, A, ws_bytes=1 << 30, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_block_select, bad, A, A, A, A, A, ws_bytes=1 << 30, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_sparse_prefill, bad, A, A, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_dense_prefill, bad, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill, bad, A, A, A, A, A, ws_bytes=1 << 40, stream=0)
+
+
+def test_null_and_misaligned_pointers():
+    cfg = _good()
+    _expect(B.PXA_ENULL, pxa.pxa_dense_prefill, cfg, A, A, 0, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_dense_prefill, cfg, A, MIS, A, A, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_proxy_pool, cfg, A, A, A, 0, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score, cfg, A, A, A + 2, stream=0)      # fp32 needs 4
+    _expect(B.PXA_EALIGN, pxa.pxa_block_select, cfg, A, A, A, A, A + 64, ws_bytes=1 << 30, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_sparse_prefill, cfg, A, A, A, A, 0, A, stream=0)
+    # NULL wins over misalignment
+    _expect(B.PXA_ENULL, pxa.pxa_prefill, cfg, MIS, A, A, 0, A, ws_bytes=1 << 40, stream=0)
+
+
+def test_workspace_too_small():
+    cfg = _good()
+    need = pxa.pxa_workspace_bytes(cfg)
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill, cfg, A, A, A, A, A, ws_bytes=need - 1, stream=0)
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_budget_estimate, cfg, A, A, A, A, A, A,
+            ws_bytes=pxa.pxa_budget_workspace_bytes(cfg) - 4, stream=0)
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_block_select, cfg, A, A, A, A, A,
+            ws_bytes=pxa.pxa_select_workspace_bytes(cfg) - 4, stream=0)
+
+
+def test_strerror_covers_codes():
+    for c in range(0, -7, -1):
+        assert pxa.pxa_strerror(c) != "unknown error code"
+    assert pxa.pxa_strerror(-99) == "unknown error code"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    cfg = _good()
+    t = torch.zeros(8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pxa.pxa_dense_prefill(cfg, t, t, t, t, stream=0)
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "block_sparse_long_proxy_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    src = f.read()
+                assert "oracle" not in src.replace("oracle_", ""), fn
