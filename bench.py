@@ -1,0 +1,278 @@
+"""Benchmark: ProxyAttn block-sparse causal prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c2]
+
+One step = one pass of the whole method over one layer of synthetic input
+already resident in HBM: proxy_pool -> proxy_score -> budget -> block_select
+-> sparse attention (pxa_prefill).  Prints one JSON line with the step latency
+(ms), the dense-attention baseline of the same kernel family, the speedup,
+the estimation share, the kept-block density, per-stage times, the roofline
+of the dominant kernel (sparse attention, MFMA-bound) and the CPU oracle timed
+on a bounded sample of the same workload (a reported baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse prefill-attn ms & speedup vs dense @128K; MFMA util on kept blocks"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+B = 128
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--gamma", type=float, default=None)
+    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="approximate CPU seconds for the oracle sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0):
+    """Time the CPU oracle on a bounded sample and scale it to the full step.
+
+    Sample: a token slice of the pooling, three query-block rows of the proxy
+    scores (scaled by causal tiles), the last-block masses of one head (scaled
+    by heads), ranking + selection of three rows (scaled by rows), and sparse
+    attention of a few (head, row) pairs on the GPU's own mask (scaled by kept
+    tiles).  `samples`: list of (h, I, kept block indices).
+    """
+    import numpy as np
+    from oracle import proxyattn as O
+    from synth import bf16_bits_to_f32
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    H, Hkv, N, d, G, nb = (cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim,
+                           cfg.num_proxies, cfg.nb)
+    f64 = lambda a: bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    scale = cfg.scale
+    est = {}
+    t_all = time.perf_counter()
+
+    ntok = min(N, 4096)
+    t = time.perf_counter()
+    O.proxy_pool(f64(x["q"][:, :ntok]), f64(x["k"][:, :ntok]), G)
+    est["pool"] = (time.perf_counter() - t) * N / ntok
+
+    rows = [nb // 8, nb // 4, nb // 2, (5 * nb) // 8, (3 * nb) // 4, (7 * nb) // 8]
+    qg = f64(x["q"][: H // G])
+    kg = f64(x["k"][: max(1, Hkv // G)])
+    t = time.perf_counter()
+    qbar0 = O.round_bf16(qg.mean(axis=0))
+    kbar0 = O.round_bf16(kg.mean(axis=0))
+    tiles = 0
+    for I in rows:
+        O.proxy_score_row(qbar0, kbar0, I, B, scale)
+        tiles += I + 1
+    est["score"] = (time.perf_counter() - t) * (G * nb * (nb + 1) / 2) / tiles
+    del qg, kg
+
+    q0, k0 = f64(x["q"][0]), f64(x["k"][0])
+    t = time.perf_counter()
+    O.last_block_masses(q0, k0, B, scale)
+    est["budget"] = (time.perf_counter() - t) * H
+    del q0, k0
+
+    srow = np.random.default_rng(1).standard_normal(nb)
+    t = time.perf_counter()
+    for I in rows:
+        O.select_row(srow, I, nb // 4)
+    est["select"] = (time.perf_counter() - t) * (G * nb) / len(rows)
+
+    done, spent = 0, 0.0
+    heads = {}
+    for h, I, cols in samples:
+        kv = h // (H // Hkv)
+        if h not in heads:
+            heads = {h: (f64(x["q"][h]), f64(x["k"][kv]), f64(x["v"][kv]))}
+        qh, kk, vv = heads[h]
+        t = time.perf_counter()
+        O.sparse_attention_row(qh, kk, vv, cols, I, B, scale)
+        spent += time.perf_counter() - t
+        done += len(cols)
+        if spent > budget_s * 0.5:
+            break
+    est["sparse"] = spent * n_kept / max(done, 1)
+    return {
+        "value": sum(est.values()) * 1e3, "unit": "ms", "cores": int(cores), "kind": "oracle",
+        "sample": (f"float64 NumPy oracle; pooling of {ntok} tokens, proxy scores of rows {rows} "
+                   f"of proxy 0, last-block masses of head 0, selection of {len(rows)} rows, "
+                   f"sparse attention of {done} kept tiles of the GPU mask; each part scaled to "
+                   f"the full step by its work units (tokens, causal tiles, heads, rows, kept tiles)"),
+        "stage_s": {k: round(v, 3) for k, v in est.items()},
+        "wall_s": round(time.perf_counter() - t_all, 2),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
+                          "part of it (the sharding design is described in DESIGN.md)",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import block_sparse_long_proxy_amd as pxa
+    from synth import get_config, generate, input_digest
+
+    wl = get_config(a.workload)
+    gamma = a.gamma if a.gamma is not None else wl.gamma
+    cfg = pxa.Config(wl.num_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.num_proxies, gamma)
+    H, Hkv, N, d, G, nb = cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim, cfg.num_proxies, cfg.nb
+    log(f"generating {wl.name}: H={H} Hkv={Hkv} N={N} d={d} G={G} gamma={gamma}")
+    t0 = time.time()
+    x = generate(wl)
+    digest = input_digest(x["q"], x["k"], x["v"])[:16]
+    log(f"generated in {time.time() - t0:.1f}s digest {digest}")
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    torch.cuda.synchronize()
+    attn = pxa.ProxyAttn(cfg)
+    o = torch.empty_like(dev["q"])
+    stream = torch.cuda.current_stream()
+
+    # whole-step timing
+    for _ in range(a.warmup):
+        attn(dev["q"], dev["k"], dev["v"], out=o)
+    torch.cuda.synchronize()
+    log("warmup done")
+    t_start = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(a.steps):
+        attn(dev["q"], dev["k"], dev["v"], out=o)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / a.steps
+    ms_step = ev0.elapsed_time(ev1) / a.steps
+    log(f"pxa_prefill: {ms_step:.3f} ms/step (host wall {wall_ms:.3f})")
+
+    # per-stage timing with the same kernels, events on the launch stream
+    L = attn.layout
+    ws = attn.ws
+    bws = ws[L.budget_ws:]
+    sws = ws[L.select_ws:]
+    names = ["pool", "score", "budget", "select", "sparse"]
+    acc = {n: 0.0 for n in names}
+    reps = max(1, a.steps)
+    for r in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        evs[0].record(stream)
+        pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
+        evs[1].record(stream)
+        pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
+        evs[2].record(stream)
+        pxa.pxa_budget_estimate(cfg, dev["q"], dev["k"], attn.scores, attn.k_h, attn.masses,
+                                bws, ws_bytes=pxa.pxa_budget_workspace_bytes(cfg))
+        evs[3].record(stream)
+        pxa.pxa_block_select(cfg, attn.scores, attn.k_h, attn.row_ptr, attn.col_idx, sws,
+                             ws_bytes=pxa.pxa_select_workspace_bytes(cfg))
+        evs[4].record(stream)
+        pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o)
+        evs[5].record(stream)
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += evs[i].elapsed_time(evs[i + 1])
+    stage = {n: acc[n] / reps for n in names}
+    log("stages ms: " + " ".join(f"{n}={v:.3f}" for n, v in stage.items()))
+
+    # dense baseline, same kernel family
+    od = torch.empty_like(dev["q"])
+    pxa.pxa_dense_prefill(cfg, dev["q"], dev["k"], dev["v"], od)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(a.dense_reps):
+        pxa.pxa_dense_prefill(cfg, dev["q"], dev["k"], dev["v"], od)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dense_ms = e0.elapsed_time(e1) / a.dense_reps
+    log(f"dense: {dense_ms:.3f} ms")
+
+    # mask statistics
+    rp = attn.row_ptr.cpu().numpy().astype(np.int64)
+    kh = attn.k_h.cpu().numpy()
+    n_kept = int(rp[-1])
+    n_diag = H * nb
+    causal_half_blocks = H * nb * nb / 2.0
+    density = (n_kept - 0.5 * n_diag) / causal_half_blocks
+    f_kept = (n_kept - n_diag) * 4.0 * B * B * d + n_diag * 2.0 * B * B * d
+    f_dense = 2.0 * N * N * d * H
+    f_score = G * (nb * (nb + 1) / 2) * 2.0 * B * B * d
+    tflops = lambda f, ms: f / (ms * 1e-3) / 1e12  # noqa: E731
+    kept_tflops = tflops(f_kept, stage["sparse"])
+    est_ms = stage["pool"] + stage["score"] + stage["budget"] + stage["select"]
+    pool_bytes = (H + Hkv + 2 * G) * N * d * 2
+    budget_bytes = Hkv * N * d * 2 + H * B * d * 2 + H * nb * B * 4 * 2
+    select_bytes = G * nb * nb * 4 + H * nb * 4 * 3 + n_kept * 4
+
+    # CPU oracle on a bounded sample (rank 0, one GPU)
+    cpu = None
+    if not a.no_cpu_baseline:
+        ci = attn.col_idx.cpu().numpy()
+        rng = np.random.default_rng(7)
+        samp = []
+        for h in sorted(rng.choice(H, size=4, replace=False).tolist()):
+            for I in rng.integers(nb // 4, nb, size=3).tolist():
+                r = h * nb + I
+                samp.append((h, I, ci[rp[r]:rp[r + 1]].astype(np.int64)))
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(cfg, x, samp, n_kept, budget_s=a.cpu_budget_s)
+        cpu["value"] = round(cpu["value"], 1)
+
+    res = {
+        "metric": METRIC, "value": round(ms_step, 3), "unit": "ms", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator, bf16, inputs resident in HBM)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": d, "seq_len": N, "block": B, "num_proxies": G, "gamma": gamma,
+                   "batch": 1, "input_sha256_16": digest},
+        "speedup_vs_dense": round(dense_ms / ms_step, 3),
+        "dense_ms": round(dense_ms, 3),
+        "estimation_ms": round(est_ms, 3),
+        "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
+        "kept_density": round(density, 4),
+        "k_h": kh.tolist(),
+        "stage_ms": {n: round(v, 4) for n, v in stage.items()},
+        "kept_block_mfma_util": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
+        "dense_mfma_util": round(tflops(f_dense, dense_ms) / PEAK_BF16_TFLOPS, 4),
+        "score_mfma_util": round(tflops(f_score, stage["score"]) / PEAK_BF16_TFLOPS, 4),
+        "hbm_gbs": {"pool": round(pool_bytes / (stage["pool"] * 1e-3) / 1e9, 1),
+                    "budget": round(budget_bytes / (stage["budget"] * 1e-3) / 1e9, 1),
+                    "select": round(select_bytes / (stage["select"] * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": "fa_prefill_kernel<128,sparse>", "bound": "mfma",
+                     "achieved": round(kept_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "host_wall_ms_per_step": round(wall_ms, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
