@@ -189,9 +189,10 @@ def main():
                                 bws, ws_bytes=pxa.pxa_budget_workspace_bytes(cfg))
         evs[3].record(stream)
         pxa.pxa_block_select(cfg, attn.scores, attn.k_h, attn.row_ptr, attn.col_idx, sws,
-                             ws_bytes=pxa.pxa_select_workspace_bytes(cfg))
+                             ws_bytes=pxa.pxa_select_workspace_bytes(cfg), row_order=attn.row_order)
         evs[4].record(stream)
-        pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o)
+        pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
+                               row_order=attn.row_order)
         evs[5].record(stream)
         torch.cuda.synchronize()
         for i, n in enumerate(names):

@@ -42,6 +42,7 @@ class ProxyAttn:
         self.k_h = view(L.k_h, H, torch.int32, (H,))
         self.row_ptr = view(L.row_ptr, H * nb + 1, torch.int32, (H * nb + 1,))
         self.col_idx = view(L.col_idx, H * nb * (nb + 1) // 2, torch.int32, (H * nb * (nb + 1) // 2,))
+        self.row_order = view(L.row_order, H * nb, torch.int32, (H * nb,))
 
     def __call__(self, q, k, v, out=None, stream=None):
         import torch

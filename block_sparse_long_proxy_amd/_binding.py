@@ -44,7 +44,7 @@ class pxa_config(ctypes.Structure):
 class pxa_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
                 ("qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx",
-                 "budget_ws", "select_ws", "total")]
+                 "row_order", "budget_ws", "select_ws", "total")]
 
 
 _P = ctypes.c_void_p
@@ -63,8 +63,8 @@ _SIGNATURES = {
     "pxa_proxy_pool": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
     "pxa_proxy_score": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
     "pxa_budget_estimate": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "pxa_block_select": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "pxa_sparse_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "pxa_block_select": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_sparse_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pxa_dense_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
 }
 
@@ -231,18 +231,21 @@ def pxa_budget_estimate(cfg: Config, q, k, scores, k_h, masses, ws, ws_bytes=Non
 
 
 def pxa_block_select(cfg: Config, scores, k_h, row_ptr, col_idx, ws, ws_bytes=None,
-                     stream=None) -> None:
+                     stream=None, row_order=None) -> None:
     _check(load_library().pxa_block_select(
         ctypes.byref(cfg.c()), _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"),
-        _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"), _tp(ws, "u8", "ws"),
-        _nbytes(ws, ws_bytes), _stream(stream)), "pxa_block_select")
+        _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
+        _tp(row_order, "i32", "row_order"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
+        _stream(stream)), "pxa_block_select")
 
 
-def pxa_sparse_prefill(cfg: Config, q, k, v, row_ptr, col_idx, o, stream=None) -> None:
+def pxa_sparse_prefill(cfg: Config, q, k, v, row_ptr, col_idx, o, stream=None,
+                       row_order=None) -> None:
     _check(load_library().pxa_sparse_prefill(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"), _tp(v, "bf16", "v"),
-        _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"), _tp(o, "bf16", "o"),
-        _stream(stream)), "pxa_sparse_prefill")
+        _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
+        _tp(row_order, "i32", "row_order"), _tp(o, "bf16", "o"), _stream(stream)),
+        "pxa_sparse_prefill")
 
 
 def pxa_dense_prefill(cfg: Config, q, k, v, o, stream=None) -> None:

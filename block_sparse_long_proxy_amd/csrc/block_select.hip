@@ -11,7 +11,8 @@
 //   select_count_kernel: one wave per (g, I); the rank of the diagonal block
 //     is a plain count of blocks ahead of it, so the row lengths (and hence
 //     row_ptr) are known without sorting.
-//   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr.
+//   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr, and
+//     a longest-first counting sort of the rows -> row_order.
 //   select_emit_kernel : one workgroup per (g, I); bitonic sort of the row's
 //     64-bit (score, index) keys in LDS gives every block's rank; each head
 //     of the group then compacts {J : rank < k or J == I} in ascending J.
@@ -45,17 +46,25 @@ __global__ __launch_bounds__(256) void select_count_kernel(const float* __restri
   }
 }
 
-// Exclusive scan of n counts into row_ptr[0..n]; one workgroup.
+// Exclusive scan of the n row lengths into row_ptr[0..n]; optionally also a
+// counting sort of the rows by length, longest first, into row_order (the
+// attention kernel's schedule: dispatched round-robin over the XCDs, a
+// longest-first list gives every XCD the same mix of long and short rows).
+// One workgroup; hist needs max_len + 1 ints of dynamic LDS.
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ row_ptr,
-                                                                   int n) {
+                                                                   int32_t* __restrict__ row_order,
+                                                                   int n, int max_len) {
   __shared__ int part[kScanThreads];
+  extern __shared__ int hist[];   // [max_len + 1]
   const int t = threadIdx.x;
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int a = min(n, t * per), b = min(n, a + per);
   int s = 0;
   for (int i = a; i < b; ++i) s += counts[i];
   part[t] = s;
+  if (row_order)
+    for (int c = t; c <= max_len; c += kScanThreads) hist[c] = 0;
   __syncthreads();
   for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele
     const int x = t >= off ? part[t - off] : 0;
@@ -69,6 +78,19 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
     run += counts[i];
   }
   if (t == kScanThreads - 1) row_ptr[n] = part[t];
+  if (!row_order) return;
+  for (int i = a; i < b; ++i) atomicAdd(&hist[min(counts[i], max_len)], 1);
+  __syncthreads();
+  if (t == 0) {   // bucket starts, longest bucket first
+    int acc = 0;
+    for (int c = max_len; c >= 0; --c) {
+      const int x = hist[c];
+      hist[c] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  for (int i = a; i < b; ++i) row_order[atomicAdd(&hist[min(counts[i], max_len)], 1)] = i;
 }
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
@@ -142,15 +164,18 @@ size_t select_ws_bytes(const LaunchArgs& a) {
 }
 
 hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
-                         int32_t* row_ptr, int32_t* col_idx, void* ws, hipStream_t stream) {
+                         int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
+                         hipStream_t stream) {
   const int nb = a.N / kBlock;
   int32_t* counts = (int32_t*)ws;
   hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,
                      k_h, counts, a.H, a.G, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, counts, row_ptr,
-                     a.H * nb);
+  const int max_len = nb + 1;   // a row keeps at most I + 1 <= nb blocks
+  hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads),
+                     row_order ? (size_t)(max_len + 1) * sizeof(int) : 0, stream, counts, row_ptr,
+                     row_order, a.H * nb, max_len);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int Pmax = 1;

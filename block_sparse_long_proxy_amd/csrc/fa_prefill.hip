@@ -19,14 +19,26 @@ template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    __bf16* __restrict__ o, int H, int Hkv, int N, float scale_log2) {
+    const int32_t* __restrict__ row_order, __bf16* __restrict__ o, int H, int Hkv, int N,
+    float scale_log2) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
   __shared__ __attribute__((aligned(16))) __bf16 vts[D * kBlock];
 
   const int nb = N / kBlock;
-  // Heavy rows first: blockIdx.x -> (I descending, h).
-  const int I = nb - 1 - (int)(blockIdx.x / H);
-  const int h = (int)(blockIdx.x % H);
+  int h, I;
+  if (!DENSE && row_order) {
+    const int r = row_order[blockIdx.x];
+    if (r < 0 || r >= H * nb) return;
+    h = r / nb;
+    I = r % nb;
+  } else {
+    // Query blocks from last (longest causal row) to first; within one query
+    // block the head index is rotated by the block so that, with workgroups
+    // dealt round-robin to the XCDs, every head visits every XCD.
+    const int step = (int)(blockIdx.x / H);
+    I = nb - 1 - step;
+    h = (int)((blockIdx.x + step) % H);
+  }
   const int kvh = h / (H / Hkv);
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
@@ -130,26 +142,26 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
 
 template <int D>
 static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, const void* v,
-                            const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
-                            hipStream_t stream) {
+                            const int32_t* row_ptr, const int32_t* col_idx,
+                            const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
   const dim3 grid(a.H * (a.N / kBlock)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   if (dense)
     hipLaunchKernelGGL((fa_prefill_kernel<D, true>), grid, block, 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2);
   else
     hipLaunchKernelGGL((fa_prefill_kernel<D, false>), grid, block, 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2);
   return hipGetLastError();
 }
 
 hipError_t launch_fa_prefill(const LaunchArgs& a, const void* q, const void* k, const void* v,
-                             const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
-                             hipStream_t stream) {
-  return a.D == 64 ? launch_fa<64>(a, q, k, v, row_ptr, col_idx, o, dense, stream)
-                   : launch_fa<128>(a, q, k, v, row_ptr, col_idx, o, dense, stream);
+                             const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
+  return a.D == 64 ? launch_fa<64>(a, q, k, v, row_ptr, col_idx, row_order, o, dense, stream)
+                   : launch_fa<128>(a, q, k, v, row_ptr, col_idx, row_order, o, dense, stream);
 }
 
 }  // namespace pxa

@@ -93,6 +93,7 @@ void layout_of(const pxa_config* c, pxa_workspace_layout* L) {
   L->k_h = take((size_t)a.H * 4);
   L->row_ptr = take(((size_t)a.H * nb + 1) * 4);
   L->col_idx = take((size_t)a.H * nb * (nb + 1) / 2 * 4);
+  L->row_order = take((size_t)a.H * nb * 4);
   L->budget_ws = take(pxa::budget_ws_bytes(a));
   L->select_ws = take(pxa::select_ws_bytes(a));
   L->total = off;
@@ -179,22 +180,27 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k, con
 }
 
 int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
-                     int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes, void* stream) {
+                     int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
+                     size_t ws_bytes, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = ptrs_ok({{scores, 4}, {k_h, 4}, {row_ptr, 4}, {col_idx, 4}, {ws, 256}}))) return rc;
+  if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
   const pxa::LaunchArgs a = args_of(cfg);
   if (ws_bytes < pxa::select_ws_bytes(a)) return PXA_EWORKSPACE;
-  return hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, ws, (hipStream_t)stream));
+  return hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, row_order, ws,
+                                   (hipStream_t)stream));
 }
 
 int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
-                       const int32_t* row_ptr, const int32_t* col_idx, void* o, void* stream) {
+                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_order,
+                       void* o, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {row_ptr, 4}, {col_idx, 4}, {o, 16}}))) return rc;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, row_ptr, col_idx, o, false,
-                                       (hipStream_t)stream));
+  if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
+  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, row_ptr, col_idx, row_order, o,
+                                       false, (hipStream_t)stream));
 }
 
 int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
@@ -202,8 +208,8 @@ int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}}))) return rc;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, nullptr, nullptr, o, true,
-                                       (hipStream_t)stream));
+  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, nullptr, nullptr, nullptr, o,
+                                       true, (hipStream_t)stream));
 }
 
 int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
@@ -224,12 +230,14 @@ int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void*
   int32_t* k_h = (int32_t*)(w + L.k_h);
   int32_t* row_ptr = (int32_t*)(w + L.row_ptr);
   int32_t* col_idx = (int32_t*)(w + L.col_idx);
+  int32_t* row_order = (int32_t*)(w + L.row_order);
   if ((rc = hip_rc(pxa::launch_proxy_pool(a, q, k, qbar, kbar, s)))) return rc;
   if ((rc = hip_rc(pxa::launch_proxy_score(a, qbar, kbar, scores, s)))) return rc;
   if ((rc = hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, w + L.budget_ws, s)))) return rc;
-  if ((rc = hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, w + L.select_ws, s))))
+  if ((rc = hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, row_order,
+                                      w + L.select_ws, s))))
     return rc;
-  return hip_rc(pxa::launch_fa_prefill(a, q, k, v, row_ptr, col_idx, o, false, s));
+  return hip_rc(pxa::launch_fa_prefill(a, q, k, v, row_ptr, col_idx, row_order, o, false, s));
 }
 
 }  // extern "C"

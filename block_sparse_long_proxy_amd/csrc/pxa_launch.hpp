@@ -26,10 +26,11 @@ hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, cons
 // ws: select_ws_bytes(a) bytes
 size_t select_ws_bytes(const LaunchArgs& a);
 hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
-                         int32_t* row_ptr, int32_t* col_idx, void* ws, hipStream_t stream);
+                         int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
+                         hipStream_t stream);
 hipError_t launch_fa_prefill(const LaunchArgs& a, const void* q, const void* k, const void* v,
-                             const int32_t* row_ptr, const int32_t* col_idx, void* o, bool dense,
-                             hipStream_t stream);
+                             const int32_t* row_ptr, const int32_t* col_idx,
+                             const int32_t* row_order, void* o, bool dense, hipStream_t stream);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

@@ -80,6 +80,7 @@ typedef struct pxa_workspace_layout {
   size_t k_h;       /* int32 [H]                         */
   size_t row_ptr;   /* int32 [H*nb + 1]                  */
   size_t col_idx;   /* int32 [H*nb*(nb+1)/2] (capacity)  */
+  size_t row_order; /* int32 [H*nb]: rows longest first  */
   size_t budget_ws; /* pxa_budget_workspace_bytes        */
   size_t select_ws; /* pxa_select_workspace_bytes        */
   size_t total;     /* == pxa_workspace_bytes            */
@@ -139,21 +140,30 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k,
 /* Step 1 ranking + final mask (section 4, step 1 "Block Ranking" with TopK,
  * and the final block sparse mask handed to FlashAttention).  Row (h, I)
  * keeps the first min(k_h[h], I+1) blocks of the group's ranking of row I
- * plus the diagonal block I.  Output is CSR over rows r = h*nb + I:
- * row_ptr[H*nb+1], col_idx[row_ptr[r] .. row_ptr[r+1]) ascending.
- * col_idx needs pxa_max_col_entries(cfg) capacity; ws: pxa_select_workspace_bytes. */
+ * plus the diagonal block I (k_h < 0 is read as 0).  Output is CSR over rows
+ * r = h*nb + I: row_ptr[H*nb+1], col_idx[row_ptr[r] .. row_ptr[r+1])
+ * ascending.  col_idx needs pxa_max_col_entries(cfg) capacity.
+ * row_order (may be NULL): receives a permutation of the H*nb rows with
+ * longer rows first, a schedule for pxa_sparse_prefill (rows of equal length
+ * come in no fixed order; it never changes any result).
+ * ws: pxa_select_workspace_bytes. */
 int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
-                     int32_t* row_ptr, int32_t* col_idx, void* ws, size_t ws_bytes,
-                     void* stream);
+                     int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Block-sparse causal attention over the CSR mask (section 4, final step; the
  * attention of section 2).  o[h][i] = sum of softmax(scale * q.k_j) v_j over
  * the keys j <= i of the kept blocks of row (h, i / B), renormalised over
  * them; fp32 online softmax, bf16 MFMA products, bf16 output (RNE).  Entries
- * of a row outside [0, I] are ignored; a row with no valid entry yields zeros. */
+ * of a row outside [0, I] are ignored; a row with no valid entry yields zeros.
+ * row_order (may be NULL): the order in which rows are handed to the GPU, a
+ * permutation of [0, H*nb) such as pxa_block_select writes (entries outside
+ * that range are skipped; a repeated row is computed twice with the same
+ * result).  NULL: query blocks from last to first, heads rotated so every
+ * head visits every XCD. */
 int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
-                       const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                       void* stream);
+                       const int32_t* row_ptr, const int32_t* col_idx,
+                       const int32_t* row_order, void* o, void* stream);
 
 /* Dense causal attention with the same kernel (every block J <= I kept):
  * the baseline the sparse path is measured against. */

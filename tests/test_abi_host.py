@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.pxa_config) == 32
-    assert ctypes.sizeof(B.pxa_workspace_layout) == 10 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(B.pxa_workspace_layout) == 11 * ctypes.sizeof(ctypes.c_size_t)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -84,7 +84,7 @@ def test_workspace_layout_is_ordered_aligned_and_sized():
     H, G, N, d, nb = 8, 2, 1024, 128, 8
     parts = [("qbar", G * N * d * 2), ("kbar", G * N * d * 2), ("scores", G * nb * nb * 4),
              ("masses", H * nb * 4), ("k_h", H * 4), ("row_ptr", (H * nb + 1) * 4),
-             ("col_idx", H * nb * (nb + 1) // 2 * 4),
+             ("col_idx", H * nb * (nb + 1) // 2 * 4), ("row_order", H * nb * 4),
              ("budget_ws", pxa.pxa_budget_workspace_bytes(cfg)),
              ("select_ws", pxa.pxa_select_workspace_bytes(cfg))]
     prev_end = 0
@@ -109,8 +109,9 @@ def test_compute_entry_points_reject_bad_config_before_launch():
     _expect(B.PXA_EINVAL, pxa.pxa_proxy_pool, bad, A, A, A, A, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_proxy_score, bad, A, A, A, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_budget_estimate, bad, A, A, A, A, A, A, ws_bytes=1 << 30, stream=0)
-    _expect(B.PXA_EINVAL, pxa.pxa_block_select, bad, A, A, A, A, A, ws_bytes=1 << 30, stream=0)
-    _expect(B.PXA_EINVAL, pxa.pxa_sparse_prefill, bad, A, A, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_block_select, bad, A, A, A, A, A, ws_bytes=1 << 30, stream=0,
+            row_order=A)
+    _expect(B.PXA_EINVAL, pxa.pxa_sparse_prefill, bad, A, A, A, A, A, A, stream=0, row_order=A)
     _expect(B.PXA_EINVAL, pxa.pxa_dense_prefill, bad, A, A, A, A, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_prefill, bad, A, A, A, A, A, ws_bytes=1 << 40, stream=0)
 
@@ -123,6 +124,9 @@ def test_null_and_misaligned_pointers():
     _expect(B.PXA_EALIGN, pxa.pxa_proxy_score, cfg, A, A, A + 2, stream=0)      # fp32 needs 4
     _expect(B.PXA_EALIGN, pxa.pxa_block_select, cfg, A, A, A, A, A + 64, ws_bytes=1 << 30, stream=0)
     _expect(B.PXA_ENULL, pxa.pxa_sparse_prefill, cfg, A, A, A, A, 0, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_sparse_prefill, cfg, A, A, A, A, A, A, stream=0, row_order=A + 2)
+    _expect(B.PXA_EALIGN, pxa.pxa_block_select, cfg, A, A, A, A, A, ws_bytes=1 << 30, stream=0,
+            row_order=A + 1)
     # NULL wins over misalignment
     _expect(B.PXA_ENULL, pxa.pxa_prefill, cfg, MIS, A, A, 0, A, ws_bytes=1 << 40, stream=0)
 

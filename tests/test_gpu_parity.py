@@ -83,12 +83,13 @@ def run_budget(cfg, dev, S):
     return kh, m
 
 
-def run_select(cfg, S, kh):
+def run_select(cfg, S, kh, with_order=False):
     rp = _empty((cfg.num_heads * cfg.nb + 1,), torch.int32)
     ci = torch.full((pxa.pxa_max_col_entries(cfg),), -7, dtype=torch.int32, device="cuda")
+    order = _empty((cfg.num_heads * cfg.nb,), torch.int32) if with_order else None
     ws = _empty((pxa.pxa_select_workspace_bytes(cfg),), torch.uint8)
-    pxa.pxa_block_select(cfg, S, kh, rp, ci, ws)
-    return rp, ci
+    pxa.pxa_block_select(cfg, S, kh, rp, ci, ws, row_order=order)
+    return (rp, ci, order) if with_order else (rp, ci)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -142,10 +143,14 @@ def test_select_parity_exact(name):
     qb, kb = run_pool(cfg, dev)
     S_dev = run_score(cfg, qb, kb)
     kh_dev, _ = run_budget(cfg, dev, S_dev)
-    rp, ci = run_select(cfg, S_dev, kh_dev)
-    rp, ci = rp.cpu().numpy(), ci.cpu().numpy()
+    rp, ci, order = run_select(cfg, S_dev, kh_dev, with_order=True)
+    rp, ci, order = rp.cpu().numpy(), ci.cpu().numpy(), order.cpu().numpy()
     S, kh = host64(S_dev), kh_dev.cpu().numpy()
     keep_ref = O.select_blocks(S, kh, cfg.num_heads)
+    n_rows = cfg.num_heads * cfg.nb
+    np.testing.assert_array_equal(np.sort(order), np.arange(n_rows))   # a permutation
+    lens = np.diff(rp)[order]
+    assert np.all(np.diff(lens) <= 0), "row_order is not longest-first"
     assert rp[0] == 0 and np.all(np.diff(rp) >= 1)
     assert rp[-1] == keep_ref.sum()
     np.testing.assert_array_equal(csr_to_keep(rp, ci, cfg.num_heads, cfg.nb), keep_ref)
@@ -175,9 +180,13 @@ def test_sparse_attention_parity_on_gpu_mask(name):
     qb, kb = run_pool(cfg, dev)
     S_dev = run_score(cfg, qb, kb)
     kh_dev, _ = run_budget(cfg, dev, S_dev)
-    rp, ci = run_select(cfg, S_dev, kh_dev)
+    rp, ci, order = run_select(cfg, S_dev, kh_dev, with_order=True)
     o = torch.empty_like(dev["q"])
-    pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], rp, ci, o)
+    pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], rp, ci, o, row_order=order)
+    o2 = torch.empty_like(dev["q"])
+    pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], rp, ci, o2)   # default schedule
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "schedule changed the result"
     keep = csr_to_keep(rp.cpu().numpy(), ci.cpu().numpy(), cfg.num_heads, cfg.nb)
     ref = O.sparse_attention(q, k, v, keep, 128, cfg.scale)
     assert_outputs_close(host64(o), ref, name)
@@ -218,11 +227,14 @@ def test_pipeline_is_deterministic():
     attn = pxa.ProxyAttn(cfg)
     o1 = attn(dev["q"], dev["k"], dev["v"]).clone()
     snap = [t.clone() for t in (attn.scores, attn.masses, attn.k_h, attn.row_ptr)]
+    nnz = int(attn.row_ptr[-1])
+    cols = attn.col_idx[:nnz].clone()
     o2 = attn(dev["q"], dev["k"], dev["v"])
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     for a, b in zip(snap, (attn.scores, attn.masses, attn.k_h, attn.row_ptr)):
         assert torch.equal(a, b)
+    assert torch.equal(cols, attn.col_idx[:nnz])
 
 
 def test_sparse_kernel_skips_invalid_entries_and_zeroes_empty_rows():
