@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle sample")
+    ap.add_argument("--profile", action="store_true",
+                    help="short pass for hardware counters: one 256 MiB device copy (counter "
+                         "calibration), one warm pxa_prefill, then --steps passes of the stages")
     return ap.parse_args()
 
 
@@ -152,6 +155,26 @@ def main():
     attn = pxa.ProxyAttn(cfg)
     o = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
+
+    if a.profile:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)      # calibration: 256 MiB read + 256 MiB written
+        attn(dev["q"], dev["k"], dev["v"], out=o)
+        L = attn.layout
+        for _ in range(a.steps):
+            pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
+            pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
+            pxa.pxa_budget_estimate(cfg, dev["q"], dev["k"], attn.scores, attn.k_h, attn.masses,
+                                    attn.ws[L.budget_ws:], ws_bytes=pxa.pxa_budget_workspace_bytes(cfg))
+            pxa.pxa_block_select(cfg, attn.scores, attn.k_h, attn.row_ptr, attn.col_idx,
+                                 attn.ws[L.select_ws:], ws_bytes=pxa.pxa_select_workspace_bytes(cfg),
+                                 row_order=attn.row_order)
+            pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
+                                   row_order=attn.row_order)
+        torch.cuda.synchronize()
+        log(f"profile pass done: kept blocks {int(attn.row_ptr[-1])}")
+        return
 
     # whole-step timing
     for _ in range(a.warmup):

@@ -10,6 +10,10 @@
 // the transposed V tile are staged through LDS and the wave computes
 //   S^T = K Q^T (32 MFMA 32x32x16), online softmax in registers,
 //   O^T += V^T P^T (32 MFMA).
+// K and V tiles are copied global -> LDS directly (no staging registers); the
+// copy of the next tile is issued before the MFMA phase it hides behind (V
+// during S + softmax, the next K during PV).  V stays row-major in LDS and is
+// read transposed with ds_read_b64_tr_b16.
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -21,8 +25,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ row_order, __bf16* __restrict__ o, int H, int Hkv, int N,
     float scale_log2) {
-  __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vts[D * kBlock];
+  __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];   // K tile, kswz layout
+  __shared__ __attribute__((aligned(16))) __bf16 vs[kBlock * D];   // V tile, vswz layout
 
   const int nb = N / kBlock;
   int h, I;
@@ -64,14 +68,32 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     beg = row_ptr[h * nb + I];
     end = row_ptr[h * nb + I + 1];
   }
+  // Next valid block at or below list position `it` (walking towards beg),
+  // or -1.  The list is visited from its end: the diagonal block, the largest
+  // valid index, comes first, so the running max is set early.
+  auto next_block = [&](int& it) -> int {
+    for (; it >= beg; --it) {
+      const int J = DENSE ? it : col_idx[it];
+      if (J >= 0 && J <= I) return J;
+    }
+    return -1;
+  };
 
-  for (int it = end - 1; it >= beg; --it) {
-    const int J = DENSE ? it : col_idx[it];
-    if (J < 0 || J > I) continue;               // uniform across the workgroup
-    __syncthreads();                              // previous tile fully consumed
-    stage_ktile<D>(kbase + (size_t)J * kBlock * D, ks);
-    stage_vtile<D>(vbase + (size_t)J * kBlock * D, vts);
-    __syncthreads();
+  // Pipeline with one K and one V tile in LDS, both filled by direct
+  // global->LDS loads: V(J) lands while S(J) and the softmax run, K(Jn)
+  // lands while O += V(J) P(J) runs.
+  int it = end - 1;
+  int J = next_block(it);
+  if (J >= 0) {
+    tile_load_lds<D, false>(kbase + (size_t)J * kBlock * D, ks);
+    tile_load_lds<D, true>(vbase + (size_t)J * kBlock * D, vs);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  while (J >= 0) {
+    --it;
+    const int Jn = next_block(it);
 
     f32x16 s[4];
     tile_scores<D>(ks, qf, s);
@@ -115,13 +137,23 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
 
+    wait_vmem();                   // this thread's part of V(J) has landed
+    __syncthreads();               // V(J) visible; every wave is done with ks
+    if (Jn >= 0) tile_load_lds<D, false>(kbase + (size_t)Jn * kBlock * D, ks);
+
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int m = 0; m < D / 32; ++m)
-          oacc[m] = mfma32(vtile_frag(vts, m, t, s2), pb[t][s2], oacc[m]);
+          oacc[m] = mfma32(vfrag_tr<D>(vs, m, t, s2), pb[t][s2], oacc[m]);
+    }
+
+    wait_vmem();                   // this thread's part of K(Jn) has landed
+    __syncthreads();               // K(Jn) visible; every wave is done with vs
+    if (Jn >= 0) tile_load_lds<D, true>(vbase + (size_t)Jn * kBlock * D, vs);
+    J = Jn;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -48,26 +48,41 @@ __device__ __forceinline__ int ktile_off(int row, int chunk) {
   return row * D + ((chunk ^ (row & (C - 1))) << 3);
 }
 
-// Copy a [128][D] bf16 tile (rows `row_stride` elements apart in global
-// memory) into the swizzled LDS layout.  All kThreads threads participate.
+// K tile staging, split so the global loads can be issued early and the LDS
+// stores done later: each thread moves kChunks 16-byte chunks of the
+// [128][D] tile (chunk c = it * kThreads + t: row c / (D/8), column c % (D/8)).
+template <int D>
+struct KStage {
+  static constexpr int kChunks = kBlock * (D / 8) / kThreads;
+  u32x4 r[kChunks];
+};
+
+template <int D>
+__device__ __forceinline__ void kstage_load(const __bf16* __restrict__ g, KStage<D>& st) {
+  constexpr int C = D / 8;
+#pragma unroll
+  for (int it = 0; it < KStage<D>::kChunks; ++it) {
+    const int c = it * kThreads + threadIdx.x;
+    st.r[it] = *reinterpret_cast<const u32x4*>(g + (size_t)(c / C) * D + (c % C) * 8);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kstage_store(const KStage<D>& st, __bf16* lds) {
+  constexpr int C = D / 8;
+#pragma unroll
+  for (int it = 0; it < KStage<D>::kChunks; ++it) {
+    const int c = it * kThreads + threadIdx.x;
+    *reinterpret_cast<u32x4*>(lds + ktile_off<D>(c / C, c % C)) = st.r[it];
+  }
+}
+
+// Whole-tile copy (load + store) for kernels that do not pipeline.
 template <int D>
 __device__ __forceinline__ void stage_ktile(const __bf16* __restrict__ g, __bf16* lds) {
-  constexpr int C = D / 8;                 // 16-byte chunks per row
-  constexpr int ITER = kBlock * C / kThreads;
-  const int t = threadIdx.x;
-  u32x4 buf[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int c = it * kThreads + t;
-    const int r = c / C, cc = c % C;
-    buf[it] = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + cc * 8);
-  }
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int c = it * kThreads + t;
-    const int r = c / C, cc = c % C;
-    *reinterpret_cast<u32x4*>(lds + ktile_off<D>(r, cc)) = buf[it];
-  }
+  KStage<D> st;
+  kstage_load<D>(g, st);
+  kstage_store<D>(st, lds);
 }
 
 // A operand (keys x d) of sub-tile `t` (32 keys) and k-step `s` (16 dims).
@@ -121,40 +136,55 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi1
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// Copy a [128 keys][D] bf16 V tile into the transposed LDS layout.  Each
-// participating thread moves one 8x8 (keys x dims) sub-block and transposes
-// it in registers.
+// V tile staging into the transposed LDS layout.  Thread t owns the 8x8
+// (keys x dims) sub-block t (key group t / (D/8), dim group t % (D/8)); for
+// D = 64 only the first 128 threads have one.  The load half fetches the 8
+// rows, the store half transposes them with byte permutes and writes 8 dims x
+// 8 keys.
 template <int D>
-__device__ __forceinline__ void stage_vtile(const __bf16* __restrict__ g, __bf16* lds) {
+struct VStage {
+  u32x4 in[8];
+};
+
+template <int D>
+__device__ __forceinline__ bool vstage_active() {
+  return threadIdx.x < (kBlock / 8) * (D / 8);
+}
+
+template <int D>
+__device__ __forceinline__ void vstage_load(const __bf16* __restrict__ g, VStage<D>& st) {
   constexpr int C = D / 8;
-  constexpr int SUB = (kBlock / 8) * C;   // 8x8 sub-blocks per tile
-  const int t = threadIdx.x;
-  for (int sb = t; sb < SUB; sb += kThreads) {
-    const int a = sb / C, b = sb % C;     // key group, dim group
-    u32x4 in[8];
+  if (!vstage_active<D>()) return;
+  const int a = threadIdx.x / C, b = threadIdx.x % C;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      in[kk] = *reinterpret_cast<const u32x4*>(g + (size_t)(8 * a + kk) * D + 8 * b);
+  for (int kk = 0; kk < 8; ++kk)
+    st.in[kk] = *reinterpret_cast<const u32x4*>(g + (size_t)(8 * a + kk) * D + 8 * b);
+}
+
+template <int D>
+__device__ __forceinline__ void vstage_store(const VStage<D>& st, __bf16* lds) {
+  constexpr int C = D / 8;
+  if (!vstage_active<D>()) return;
+  const int a = threadIdx.x / C, b = threadIdx.x % C;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // out row: dim 8b+e, keys 8a..8a+7 -> 4 u32 words of 2 keys each
-      u32x2 w0, w1;
-      const int word = e >> 1;
-      if (e & 1) {
-        w0[0] = pack_hi(in[0][word], in[1][word]);
-        w0[1] = pack_hi(in[2][word], in[3][word]);
-        w1[0] = pack_hi(in[4][word], in[5][word]);
-        w1[1] = pack_hi(in[6][word], in[7][word]);
-      } else {
-        w0[0] = pack_lo(in[0][word], in[1][word]);
-        w0[1] = pack_lo(in[2][word], in[3][word]);
-        w1[0] = pack_lo(in[4][word], in[5][word]);
-        w1[1] = pack_lo(in[6][word], in[7][word]);
-      }
-      const int d = 8 * b + e;
-      *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a)) = w0;
-      *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a + 1)) = w1;
+  for (int e = 0; e < 8; ++e) {
+    // out row: dim 8b+e, keys 8a..8a+7 -> 4 u32 words of 2 keys each
+    u32x2 w0, w1;
+    const int word = e >> 1;
+    if (e & 1) {
+      w0[0] = pack_hi(st.in[0][word], st.in[1][word]);
+      w0[1] = pack_hi(st.in[2][word], st.in[3][word]);
+      w1[0] = pack_hi(st.in[4][word], st.in[5][word]);
+      w1[1] = pack_hi(st.in[6][word], st.in[7][word]);
+    } else {
+      w0[0] = pack_lo(st.in[0][word], st.in[1][word]);
+      w0[1] = pack_lo(st.in[2][word], st.in[3][word]);
+      w1[0] = pack_lo(st.in[4][word], st.in[5][word]);
+      w1[1] = pack_lo(st.in[6][word], st.in[7][word]);
     }
+    const int d = 8 * b + e;
+    *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a)) = w0;
+    *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a + 1)) = w1;
   }
 }
 
@@ -198,6 +228,76 @@ __device__ __forceinline__ uint32_t float_order_key(float f) {
 // then block index ascending.
 __device__ __forceinline__ uint64_t rank_key(float s, uint32_t J) {
   return ((uint64_t)(~float_order_key(s)) << 32) | (uint64_t)J;
+}
+
+}  // namespace pxa
+
+namespace pxa {
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS tile copies (global_load_lds_dwordx4: lane l of a wave
+// writes its 16 bytes at LDS base + 16 l, so one instruction fills 1 KB, i.e.
+// 1024 / (2 D) consecutive rows).  The source address of each lane is chosen
+// so that the LDS image is the XOR-swizzled layout the readers expect; no
+// registers and no VALU work are spent on staging.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) short lds_s16;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Swizzle of 16-byte chunks for the K tile (MFMA A operand read with 16-byte
+// loads, 32 consecutive rows per wave): chunk ^ (row mod chunks-per-row).
+template <int D>
+__device__ __forceinline__ int kswz(int row) { return row & (D / 8 - 1); }
+// Swizzle for the V tile read with ds_read_b64_tr_b16 (16 lanes read 4
+// consecutive rows x 32 bytes): rows 4k..4k+3 land on disjoint bank groups.
+template <int D>
+__device__ __forceinline__ int vswz(int row) { return (row & 3) * (D / 32); }
+
+template <int D, bool IS_V>
+__device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf16* lds) {
+  constexpr int C = D / 8;                    // 16-byte chunks per row
+  constexpr int ROWS = 64 / C;                // rows per wave instruction
+  constexpr int INSTS = kBlock / ROWS / kWaves;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int it = 0; it < INSTS; ++it) {
+    const int blk = it * kWaves + w;
+    const int row = blk * ROWS + l / C;
+    const int phys = l % C;
+    const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
+    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * D + logical * 8),
+                                     (lds_void*)(lds + blk * ROWS * D), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Element offset of (row, col) in a swizzled V tile.
+template <int D>
+__device__ __forceinline__ int vtile_off(int row, int col) {
+  return row * D + (((col >> 3) ^ vswz<D>(row)) << 3) + (col & 7);
+}
+
+// A operand of O^T += V^T . P^T from a row-major (keys x dims) V tile, read
+// with the transposing LDS load: lane (group g16 = (l/16)%2, i = l%16) gets
+// dim 32 m + 16 g16 + i and keys kb..kb+3 from one read, kb+8..kb+11 from the
+// second, kb = 32 t + 16 s2 + 4 hi -- the keys the C layout of S^T sub-tile t
+// gives this lane in registers 8 s2 .. 8 s2 + 7.
+template <int D>
+__device__ __forceinline__ bf16x8 vfrag_tr(const __bf16* vs, int m, int t, int s2) {
+  const int l = threadIdx.x & 63;
+  const int i = l & 15, g16 = (l >> 4) & 1, hi = l >> 5;
+  const int col = 32 * m + 16 * g16 + 4 * (i & 3);
+  const int row = 32 * t + 16 * s2 + 4 * hi + (i >> 2);
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((lds_s16*)vs + vtile_off<D>(row, col)));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)((lds_s16*)vs + vtile_off<D>(row + 8, col)));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 }  // namespace pxa
