@@ -19,6 +19,84 @@
 
 namespace pxa {
 
+// Online-softmax update for one 128-key tile whose logits are in s[4]
+// (S^T layout: this lane's query, 64 of the tile's keys).  Masked entries are
+// -inf.  Returns the bf16 probabilities in the B-operand layout of the PV
+// MFMA and rescales the running output when the running max moved.
+template <int D>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[4], bf16x8 (&pb)[4][2],
+                                               f32x16 (&oacc)[D / 32], float& m_run,
+                                               float& l_run, float scale_log2) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(m_run, mx);
+  // m_new is finite once any unmasked key has been seen (always true after
+  // the diagonal block, which comes first when present).
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  // v_exp_f32 directly: probabilities below 2^-126 flush to zero.
+  const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+  m_run = m_new;
+  const float mb = m_use * scale_log2;
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mb));
+      lsum += p;
+      pb[t][r >> 3][r & 7] = (__bf16)p;
+    }
+  }
+  l_run = fmaf(l_run, alpha, lsum);
+  if (__any(alpha != 1.0f)) {      // wave-uniform: skip when no max moved
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
+  }
+}
+
+// One pipeline step on key block J (tiles already in LDS / landing): S, the
+// softmax, then O += V P, issuing the copies of block Jn (< 0: none).
+template <int D, bool DIAG>
+__device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_lds, __bf16* ks,
+                                        __bf16* vs, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
+                                        float scale_log2, int qloc, const __bf16* knext,
+                                        const __bf16* vnext) {
+  f32x16 s[4];
+  tile_scores<D>(ks_lds, qf, s);
+  if (DIAG) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (acc_key(t, r) > qloc) s[t][r] = -INFINITY;
+  }
+  bf16x8 pb[4][2];
+  softmax_update<D>(s, pb, oacc, m_run, l_run, scale_log2);
+
+  wait_vmem();                   // this thread's part of V(J) has landed
+  __syncthreads();               // V(J) visible; every wave is done with the K tile
+  if (knext) tile_load_lds<D, false>(knext, ks);
+
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        oacc[m] = mfma32(vfrag_tr<D>(vs_lds, m, t, s2), pb[t][s2], oacc[m]);
+
+  wait_vmem();                   // this thread's part of K(Jn) has landed
+  __syncthreads();               // K(Jn) visible; every wave is done with the V tile
+  if (vnext) tile_load_lds<D, true>(vnext, vs);
+}
+
 template <int D, bool DENSE>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -50,6 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
 
   const __bf16* kbase = k + (size_t)kvh * N * D;
   const __bf16* vbase = v + (size_t)kvh * N * D;
+  constexpr size_t kTile = (size_t)kBlock * D;
 
   bf16x8 qf[D / 16];
   load_qfrag<D>(q + ((size_t)h * N + (size_t)I * kBlock + qloc) * D, qf);
@@ -70,7 +149,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   }
   // Next valid block at or below list position `it` (walking towards beg),
   // or -1.  The list is visited from its end: the diagonal block, the largest
-  // valid index, comes first, so the running max is set early.
+  // valid index, comes first, so the running max is set early and only that
+  // first step needs the causal mask.
   auto next_block = [&](int& it) -> int {
     for (; it >= beg; --it) {
       const int J = DENSE ? it : col_idx[it];
@@ -79,80 +159,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     return -1;
   };
 
-  // Pipeline with one K and one V tile in LDS, both filled by direct
-  // global->LDS loads: V(J) lands while S(J) and the softmax run, K(Jn)
-  // lands while O += V(J) P(J) runs.
   int it = end - 1;
   int J = next_block(it);
   if (J >= 0) {
-    tile_load_lds<D, false>(kbase + (size_t)J * kBlock * D, ks);
-    tile_load_lds<D, true>(vbase + (size_t)J * kBlock * D, vs);
+    tile_load_lds<D, false>(kbase + (size_t)J * kTile, ks);
+    tile_load_lds<D, true>(vbase + (size_t)J * kTile, vs);
   }
   wait_vmem();
   __syncthreads();
 
+  if (J == I) {
+    --it;
+    const int Jn = next_block(it);
+    fa_step<D, true>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
+                     Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
+                     Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr);
+    J = Jn;
+  }
   while (J >= 0) {
     --it;
     const int Jn = next_block(it);
-
-    f32x16 s[4];
-    tile_scores<D>(ks, qf, s);
-
-    if (J == I) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_key(t, r) > qloc) s[t][r] = -INFINITY;
-    }
-
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    // m_new is finite once any unmasked key has been seen (always true after
-    // the diagonal block, which comes first when present).
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * scale_log2);
-    m_run = m_new;
-    const float mb = m_use * scale_log2;
-
-    bf16x8 pb[4][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(fmaf(s[t][r], scale_log2, -mb));
-        lsum += p;
-        pb[t][r >> 3][r & 7] = (__bf16)p;
-      }
-    }
-    l_run = fmaf(l_run, alpha, lsum);
-#pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[m][r] *= alpha;
-
-    wait_vmem();                   // this thread's part of V(J) has landed
-    __syncthreads();               // V(J) visible; every wave is done with ks
-    if (Jn >= 0) tile_load_lds<D, false>(kbase + (size_t)Jn * kBlock * D, ks);
-
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m)
-          oacc[m] = mfma32(vfrag_tr<D>(vs, m, t, s2), pb[t][s2], oacc[m]);
-    }
-
-    wait_vmem();                   // this thread's part of K(Jn) has landed
-    __syncthreads();               // K(Jn) visible; every wave is done with vs
-    if (Jn >= 0) tile_load_lds<D, true>(vbase + (size_t)Jn * kBlock * D, vs);
+    fa_step<D, false>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
+                      Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
+                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr);
     J = Jn;
   }
 
