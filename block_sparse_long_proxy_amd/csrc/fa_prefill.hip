@@ -151,9 +151,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   // or -1.  The list is visited from its end: the diagonal block, the largest
   // valid index, comes first, so the running max is set early and only that
   // first step needs the causal mask.
+  // (Indices are made explicitly wave-uniform so the entries come through the
+  // scalar cache and never wait on the vector-memory counter, which also
+  // counts the tile copies in flight.)
   auto next_block = [&](int& it) -> int {
     for (; it >= beg; --it) {
-      const int J = DENSE ? it : col_idx[it];
+      const int J = DENSE ? it : __builtin_amdgcn_readfirstlane(col_idx[__builtin_amdgcn_readfirstlane(it)]);
       if (J >= 0 && J <= I) return J;
     }
     return -1;

@@ -6,74 +6,139 @@
 // Causal prefill: in the diagonal block only keys j <= i count; blocks above
 // the diagonal get -inf.
 //
-// One workgroup per (proxy g, query block I), 4 waves x 32 queries, proxy
-// queries held as MFMA B operands in registers; key tiles J = 0..I stream
-// through LDS.  The max is taken in registers, across the wave with shuffles
-// and across the 4 waves through a double-buffered LDS slot, so each tile
-// costs one barrier.
+// One workgroup per proxy g and pair of query-block rows (I, I-1).  Key tiles
+// J = 0..I stream through a three-deep LDS ring filled by direct global->LDS
+// copies (tiles J+1 and J+2 are in flight while J is used).  Each of the eight
+// waves computes 32 keys of the tile against all 128 proxy queries of its row,
+// which stay in registers as MFMA B operands, so every K fragment read from
+// LDS feeds four MFMAs.  The max is taken in registers, across the wave with
+// shuffles and across the four waves of a row through a double-buffered LDS
+// slot.
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
 namespace pxa {
 
+constexpr int kScoreWaves = 8;                 // two rows x four key slices
+constexpr int kScoreThreads = 64 * kScoreWaves;
+constexpr int kScoreBufs = 3;                  // K tiles in flight / in use
+
+// Direct global->LDS copy of one [128][D] K tile by all kScoreThreads threads
+// (the tile_load_lds scheme with eight waves).
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
+__device__ __forceinline__ void score_tile_load(const __bf16* __restrict__ g, __bf16* lds) {
+  constexpr int C = D / 8;
+  constexpr int ROWS = 64 / C;
+  constexpr int INSTS = kBlock / ROWS / kScoreWaves;
+  static_assert((kScoreWaves * ROWS) % 16 == 0, "swizzle must repeat every instruction");
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row0 = w * ROWS + l / C;
+  const int logical = (l % C) ^ kswz<D>(row0);
+  const uint32_t voff = (uint32_t)((l / C) * D + logical * 8) * 2u;
+  const uint32_t lbase = lds_addr(lds) + (uint32_t)(w * ROWS * D * 2);
+#pragma unroll
+  for (int it = 0; it < INSTS; ++it) {
+    const int blk_row = (it * kScoreWaves + w) * ROWS;
+    lds_dma16(g + (size_t)blk_row * D, voff, lbase + (uint32_t)(it * kScoreWaves * ROWS * D * 2));
+  }
+}
+
+// Waves 0-3 serve row I, waves 4-7 row I-1 (absent when I == 0).  Both rows
+// need key tiles 0..I-1, so each staged tile feeds twice the MFMA work.
+template <int D>
+__global__ __launch_bounds__(kScoreThreads, 1) void proxy_score_kernel(
     const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
     int G, int N, float scale) {
-  __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
-  __shared__ float wmax[2][kWaves];
+  __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
+  __shared__ float wmax[2][kScoreWaves];
 
   const int nb = N / kBlock;
-  const int I = nb - 1 - (int)(blockIdx.x / G);
+  const int pair = (int)(blockIdx.x / G);        // longest rows first
   const int g = (int)(blockIdx.x % G);
+  const int I = nb - 1 - 2 * pair;               // top row of the pair
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
-  const int qloc = 32 * w + (l & 31);
+  const int rsel = w >> 2;                       // 0: row I, 1: row I-1
+  const int ws = w & 3;                          // key slice 32 ws .. 32 ws + 31
+  const int myI = I - rsel;
+  const bool active = myI >= 0;
+  constexpr size_t kTile = (size_t)kBlock * D;
+  constexpr int kLoadsPerTile = kBlock / (64 / (D / 8)) / kScoreWaves;
 
-  bf16x8 qf[D / 16];
-  load_qfrag<D>(qbar + ((size_t)g * N + (size_t)I * kBlock + qloc) * D, qf);
-  const __bf16* kb = kbar + (size_t)g * N * D;
-  float* srow = scores + ((size_t)g * nb + I) * nb;
-
-  for (int J = I + 1 + threadIdx.x; J < nb; J += kThreads) srow[J] = -INFINITY;
-
-  for (int J = 0; J <= I; ++J) {
-    __syncthreads();
-    if (J > 0 && threadIdx.x == 0) {
-      const float* wm = wmax[(J - 1) & 1];
-      srow[J - 1] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) * scale;
-    }
-    stage_ktile<D>(kb + (size_t)J * kBlock * D, ks);
-    __syncthreads();
-
-    f32x16 s[4];
-    tile_scores<D>(ks, qf, s);
-    float mx = -INFINITY;
-    if (J == I) {
+  bf16x8 qf[4][D / 16];
+  if (active) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (acc_key(t, r) <= qloc) mx = fmaxf(mx, s[t][r]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-    }
-    mx = wave_max(mx);
-    if (l == 0) wmax[J & 1][w] = mx;
+    for (int qs = 0; qs < 4; ++qs)
+      load_qfrag<D>(qbar + ((size_t)g * N + (size_t)myI * kBlock + 32 * qs + (l & 31)) * D, qf[qs]);
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float* wm = wmax[I & 1];
-    srow[I] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) * scale;
+  const __bf16* kb = kbar + (size_t)g * N * D;
+  float* srow0 = scores + ((size_t)g * nb + I) * nb;
+  for (int J = I + 1 + threadIdx.x; J < nb; J += kScoreThreads) srow0[J] = -INFINITY;
+  if (I >= 1) {
+    float* srow1 = srow0 - nb;
+    for (int J = I + threadIdx.x; J < nb; J += kScoreThreads) srow1[J] = -INFINITY;
+  }
+
+  // prologue: tiles 0 .. kScoreBufs-2 in flight
+#pragma unroll
+  for (int p = 0; p < kScoreBufs - 1; ++p)
+    if (p <= I) score_tile_load<D>(kb + (size_t)p * kTile, kt[p]);
+  const int hi = l >> 5;
+  for (int J = 0; J <= I; ++J) {
+    // wait for this thread's part of tile J; tile J+1 may stay in flight
+    if (J + 1 <= I)
+      wait_vmem_le<kLoadsPerTile>();
+    else
+      wait_vmem();
+    __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
+    if (J + kScoreBufs - 1 <= I)
+      score_tile_load<D>(kb + (size_t)(J + kScoreBufs - 1) * kTile,
+                         kt[(J + kScoreBufs - 1) % kScoreBufs]);
+    float mx = -INFINITY;
+    if (active && J <= myI) {
+      const __bf16* cur = kt[J % kScoreBufs];
+      f32x16 acc[4];
+#pragma unroll
+      for (int qs = 0; qs < 4; ++qs) acc[qs] = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const bf16x8 a = ktile_frag<D>(cur, ws, s);
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) acc[qs] = mfma32(a, qf[qs][s], acc[qs]);
+      }
+      if (J == myI) {   // causal: key 32 ws + row(r) must not exceed query 32 qs + l%32
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * ws + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key <= 32 * qs + (l & 31)) mx = fmaxf(mx, acc[qs][r]);
+          }
+      } else {
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[qs][r]);
+      }
+      mx = wave_max(mx);
+    }
+    if (l == 0) wmax[J & 1][w] = mx;
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const int rr = threadIdx.x;                // 0: row I, 1: row I-1
+      if (I - rr >= 0 && J <= I - rr) {
+        const float* wm = wmax[J & 1] + 4 * rr;
+        scores[((size_t)g * nb + (I - rr)) * nb + J] =
+            fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) * scale;
+      }
+    }
   }
 }
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,
                               float* scores, hipStream_t stream) {
-  const dim3 grid(a.G * (a.N / kBlock)), block(kThreads);
+  const int nb = a.N / kBlock;
+  const dim3 grid(a.G * ((nb + 1) / 2)), block(kScoreThreads);
   if (a.D == 64)
     hipLaunchKernelGGL(proxy_score_kernel<64>, grid, block, 0, stream, (const __bf16*)qbar,
                        (const __bf16*)kbar, scores, a.G, a.N, a.scale);

@@ -253,24 +253,70 @@ __device__ __forceinline__ int kswz(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int vswz(int row) { return (row & 3) * (D / 32); }
 
+// One global_load_lds_dwordx4 in scalar-base mode: this lane's 16 bytes at
+// gbase + voff go to LDS byte address lds_wave_base + 16 * lane.  Issued
+// through asm so the compiler does not drain every pending copy before
+// unrelated LDS reads (it cannot tell the destination tiles apart).  No
+// register is written.  Ordering is explicit: every LDS access to a copy's
+// destination tile is separated from the copy by a workgroup barrier (reads
+// of the old contents before it; reads of the new contents after
+// wait_vmem*() and the next barrier), and volatile asm keeps its place
+// relative to those waits and barriers.  There is deliberately no "memory"
+// clobber: it would forbid scalar loads of read-only arguments.
+__device__ __forceinline__ void lds_dma16(const void* gbase_in, uint32_t voff, uint32_t lds_in) {
+  // both bases are wave-uniform; readfirstlane puts them in SGPRs
+  const uint64_t gb = (uint64_t)(uintptr_t)gbase_in;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)gb);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
+  const void* gbase = (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const uint32_t lds_wave_base = __builtin_amdgcn_readfirstlane(lds_in);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds_wave_base), "v"(voff), "s"(gbase)
+      : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Copy one [128][D] bf16 tile (rows D elements apart at g, wave-uniform) into
+// the swizzled LDS image at lds.  Instruction it of wave w fills rows
+// (it * kWaves + w) * ROWS .. +ROWS-1; the swizzle term depends on the row
+// only modulo 4 * ROWS, which is the same for every instruction of a wave, so
+// one per-lane byte offset serves all of them and only the scalar base moves.
 template <int D, bool IS_V>
 __device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf16* lds) {
   constexpr int C = D / 8;                    // 16-byte chunks per row
   constexpr int ROWS = 64 / C;                // rows per wave instruction
   constexpr int INSTS = kBlock / ROWS / kWaves;
+  static_assert((kWaves * ROWS) % 16 == 0, "swizzle must repeat every instruction");
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int row0 = w * ROWS + l / C;          // row of instruction 0
+  const int logical = (l % C) ^ (IS_V ? vswz<D>(row0) : kswz<D>(row0));
+  const uint32_t voff = (uint32_t)((l / C) * D + logical * 8) * 2u;   // bytes, same for all it
+  const uint32_t lbase = lds_addr(lds) + (uint32_t)(w * ROWS * D * 2);
 #pragma unroll
   for (int it = 0; it < INSTS; ++it) {
-    const int blk = it * kWaves + w;
-    const int row = blk * ROWS + l / C;
-    const int phys = l % C;
-    const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
-    __builtin_amdgcn_global_load_lds((const void*)(g + (size_t)row * D + logical * 8),
-                                     (lds_void*)(lds + blk * ROWS * D), 16, 0, 0);
+    const int blk_row = (it * kWaves + w) * ROWS;
+    lds_dma16(g + (size_t)blk_row * D, voff, lbase + (uint32_t)(it * kWaves * ROWS * D * 2));
   }
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+
+// s_waitcnt vmcnt(N) with the other counters unconstrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).  Vector
+// memory operations complete in issue order, so this waits for all but the N
+// most recent loads of this thread.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 // Element offset of (row, col) in a swizzled V tile.
 template <int D>
