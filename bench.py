@@ -49,6 +49,42 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fa_prefill_sparse_c2.md")
+KERNEL_SOURCES = ["block_sparse_long_proxy_amd/csrc/fa_prefill.hip",
+                  "block_sparse_long_proxy_amd/csrc/pxa_device.hpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload):
+    """HBM bytes per sparse-attention launch from the committed rocprofv3
+    counter summary, or None if it is missing, for another workload, or taken
+    on different kernel sources."""
+    try:
+        with open(PROFILE_SUMMARY) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for line in lines:
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv.setdefault(k.strip(), v.strip())
+    if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0):
     """Time the CPU oracle on a bounded sample and scale it to the full step.
 
@@ -291,7 +327,7 @@ def main():
         "roofline": {"kernel": "fa_prefill_kernel<128,sparse>", "bound": "mfma",
                      "achieved": round(kept_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": profiled_traffic(wl.name)},
         "cpu_baseline": cpu,
         "host_wall_ms_per_step": round(wall_ms, 3),
     }
