@@ -114,12 +114,20 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     h = r / nb;
     I = r % nb;
   } else {
-    // Query blocks from last (longest causal row) to first; within one query
-    // block the head index is rotated by the block so that, with workgroups
-    // dealt round-robin to the XCDs, every head visits every XCD.
+    // Query blocks from last (longest causal row) to first.  Workgroups are
+    // dealt round-robin to the 8 XCDs (XCD = blockIdx mod 8).  Dense: XCD x
+    // gets the consecutive heads [x H/8, (x+1) H/8), i.e. whole KV-head groups
+    // when H/8 is a multiple of H/Hkv, so heads reading the same K/V tiles at
+    // the same time share that XCD's L2.  Sparse without a schedule: heads
+    // have unequal work, so the head index is rotated by the query block and
+    // every head visits every XCD.
     const int step = (int)(blockIdx.x / H);
     I = nb - 1 - step;
-    h = (int)((blockIdx.x + step) % H);
+    const int j = (int)(blockIdx.x % H);
+    if (DENSE)
+      h = (H % 8 == 0) ? (j % 8) * (H / 8) + j / 8 : j;
+    else
+      h = (j + step) % H;
   }
   const int kvh = h / (H / Hkv);
   const int w = threadIdx.x >> 6;

@@ -284,27 +284,32 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Copy one [128][D] bf16 tile (rows D elements apart at g, wave-uniform) into
-// the swizzled LDS image at lds.  Instruction it of wave w fills rows
-// (it * kWaves + w) * ROWS .. +ROWS-1; the swizzle term depends on the row
-// only modulo 4 * ROWS, which is the same for every instruction of a wave, so
-// one per-lane byte offset serves all of them and only the scalar base moves.
-template <int D, bool IS_V>
+// the swizzled LDS image at lds, using NW waves.  Instruction it of wave w
+// fills rows (it * NW + w) * ROWS .. +ROWS-1; the swizzle term depends on the
+// row only modulo NW * ROWS (a multiple of 16), which is the same for every
+// instruction of a wave, so one per-lane byte offset serves all of them and
+// only the scalar base moves.
+template <int D, bool IS_V, int NW = kWaves>
 __device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf16* lds) {
   constexpr int C = D / 8;                    // 16-byte chunks per row
   constexpr int ROWS = 64 / C;                // rows per wave instruction
-  constexpr int INSTS = kBlock / ROWS / kWaves;
-  static_assert((kWaves * ROWS) % 16 == 0, "swizzle must repeat every instruction");
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  constexpr int INSTS = kBlock / ROWS / NW;
+  static_assert((NW * ROWS) % 16 == 0, "swizzle must repeat every instruction");
+  const int w = (threadIdx.x >> 6) % NW, l = threadIdx.x & 63;
   const int row0 = w * ROWS + l / C;          // row of instruction 0
   const int logical = (l % C) ^ (IS_V ? vswz<D>(row0) : kswz<D>(row0));
   const uint32_t voff = (uint32_t)((l / C) * D + logical * 8) * 2u;   // bytes, same for all it
   const uint32_t lbase = lds_addr(lds) + (uint32_t)(w * ROWS * D * 2);
 #pragma unroll
   for (int it = 0; it < INSTS; ++it) {
-    const int blk_row = (it * kWaves + w) * ROWS;
-    lds_dma16(g + (size_t)blk_row * D, voff, lbase + (uint32_t)(it * kWaves * ROWS * D * 2));
+    const int blk_row = (it * NW + w) * ROWS;
+    lds_dma16(g + (size_t)blk_row * D, voff, lbase + (uint32_t)(it * NW * ROWS * D * 2));
   }
 }
+
+// Copies one tile costs each thread when NW waves share it.
+template <int D, int NW>
+constexpr int tile_loads_per_thread() { return kBlock / (64 / (D / 8)) / NW; }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 
