@@ -41,17 +41,25 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], bf16x8 (&pb)[4][2
   const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
   m_run = m_new;
   const float mb = m_use * scale_log2;
-  float lsum = 0.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mb));
-      lsum += p;
-      pb[t][r >> 3][r & 7] = (__bf16)p;
-    }
-  }
-  l_run = fmaf(l_run, alpha, lsum);
+    for (int r = 0; r < 16; ++r)
+      pb[t][r >> 3][r & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mb));
+  // Row sum of the bf16 probabilities the PV product uses (two per dot2), so
+  // the normaliser matches the numerator's weights exactly.
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ls0 = 0.f, ls1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) {
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][s2][e], pb[t][s2][e + 1]}, ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[t][s2][e + 2], pb[t][s2][e + 3]}, ones, ls1, false);
+      }
+  l_run = fmaf(l_run, alpha, ls0 + ls1);
   if (__any(alpha != 1.0f)) {      // wave-uniform: skip when no max moved
 #pragma unroll
     for (int m = 0; m < D / 32; ++m)
@@ -129,7 +137,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     else
       h = (j + step) % H;
   }
-  const int kvh = h / (H / Hkv);
+  // wave-uniform indices in scalar registers, so tile addresses stay scalar
+  h = __builtin_amdgcn_readfirstlane(h);
+  I = __builtin_amdgcn_readfirstlane(I);
+  const int kvh = __builtin_amdgcn_readfirstlane(h / (H / Hkv));
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int qloc = 32 * w + (l & 31);          // query index inside block I

@@ -12,8 +12,9 @@
 // waves computes 32 keys of the tile against all 128 proxy queries of its row,
 // which stay in registers as MFMA B operands, so every K fragment read from
 // LDS feeds four MFMAs.  The max is taken in registers, across the wave with
-// shuffles and across the four waves of a row through a double-buffered LDS
-// slot.
+// DPP moves (no LDS round trips), and kept in lane J mod 64; every 64 tiles the
+// four waves of a row combine their maxima through LDS and store them as one
+// coalesced run, so the only per-tile barrier is the one guarding the ring.
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -31,7 +32,9 @@ __device__ __forceinline__ void score_tile_load(const __bf16* __restrict__ g, __
   constexpr int ROWS = 64 / C;
   constexpr int INSTS = kBlock / ROWS / kScoreWaves;
   static_assert((kScoreWaves * ROWS) % 16 == 0, "swizzle must repeat every instruction");
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = threadIdx.x & 63;
+  g = uniform_ptr(g);
   const int row0 = w * ROWS + l / C;
   const int logical = (l % C) ^ kswz<D>(row0);
   const uint32_t voff = (uint32_t)((l / C) * D + logical * 8) * 2u;
@@ -44,19 +47,22 @@ __device__ __forceinline__ void score_tile_load(const __bf16* __restrict__ g, __
 }
 
 // Waves 0-3 serve row I, waves 4-7 row I-1 (absent when I == 0).  Both rows
-// need key tiles 0..I-1, so each staged tile feeds twice the MFMA work.
+// need key tiles 0..I-1, so each staged tile feeds twice the MFMA work.  The
+// block maximum of tile J stays in lane J mod 64 of each wave; every 64 tiles
+// the four slices of a row are combined through LDS and stored as one
+// coalesced run of scores.
 template <int D>
 __global__ __launch_bounds__(kScoreThreads, 1) void proxy_score_kernel(
     const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
     int G, int N, float scale) {
   __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
-  __shared__ float wmax[2][kScoreWaves];
+  __shared__ float wm[2][kScoreWaves][64];       // per-wave maxima of one 64-tile chunk
 
   const int nb = N / kBlock;
   const int pair = (int)(blockIdx.x / G);        // longest rows first
   const int g = (int)(blockIdx.x % G);
   const int I = nb - 1 - 2 * pair;               // top row of the pair
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = threadIdx.x & 63;
   const int rsel = w >> 2;                       // 0: row I, 1: row I-1
   const int ws = w & 3;                          // key slice 32 ws .. 32 ws + 31
@@ -71,19 +77,31 @@ __global__ __launch_bounds__(kScoreThreads, 1) void proxy_score_kernel(
     for (int qs = 0; qs < 4; ++qs)
       load_qfrag<D>(qbar + ((size_t)g * N + (size_t)myI * kBlock + 32 * qs + (l & 31)) * D, qf[qs]);
   }
-  const __bf16* kb = kbar + (size_t)g * N * D;
+  const __bf16* kb = uniform_ptr(kbar + (size_t)g * N * D);
   float* srow0 = scores + ((size_t)g * nb + I) * nb;
   for (int J = I + 1 + threadIdx.x; J < nb; J += kScoreThreads) srow0[J] = -INFINITY;
   if (I >= 1) {
     float* srow1 = srow0 - nb;
     for (int J = I + threadIdx.x; J < nb; J += kScoreThreads) srow1[J] = -INFINITY;
   }
+  // Threads 0..127: combine chunk c (tiles 64c .. 64c+63) of rows I and I-1.
+  auto store_chunk = [&](int c) {
+    if (threadIdx.x < 128) {
+      const int rr = threadIdx.x >> 6;
+      const int J = 64 * c + l;
+      if (J <= I - rr) {
+        const float* p = &wm[c & 1][4 * rr][l];
+        srow0[J - (size_t)rr * nb] = fmaxf(fmaxf(p[0], p[64]), fmaxf(p[128], p[192])) * scale;
+      }
+    }
+  };
 
   // prologue: tiles 0 .. kScoreBufs-2 in flight
 #pragma unroll
   for (int p = 0; p < kScoreBufs - 1; ++p)
     if (p <= I) score_tile_load<D>(kb + (size_t)p * kTile, kt[p]);
   const int hi = l >> 5;
+  float keep = -INFINITY;                        // this wave's max of tile J, in lane J mod 64
   for (int J = 0; J <= I; ++J) {
     // wait for this thread's part of tile J; tile J+1 may stay in flight
     if (J + 1 <= I)
@@ -94,6 +112,7 @@ __global__ __launch_bounds__(kScoreThreads, 1) void proxy_score_kernel(
     if (J + kScoreBufs - 1 <= I)
       score_tile_load<D>(kb + (size_t)(J + kScoreBufs - 1) * kTile,
                          kt[(J + kScoreBufs - 1) % kScoreBufs]);
+    if (J > 0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
     float mx = -INFINITY;
     if (active && J <= myI) {
       const __bf16* cur = kt[J % kScoreBufs];
@@ -120,19 +139,16 @@ __global__ __launch_bounds__(kScoreThreads, 1) void proxy_score_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[qs][r]);
       }
-      mx = wave_max(mx);
+      mx = wave_max_uniform(mx);
     }
-    if (l == 0) wmax[J & 1][w] = mx;
-    __syncthreads();
-    if (threadIdx.x < 2) {
-      const int rr = threadIdx.x;                // 0: row I, 1: row I-1
-      if (I - rr >= 0 && J <= I - rr) {
-        const float* wm = wmax[J & 1] + 4 * rr;
-        scores[((size_t)g * nb + (I - rr)) * nb + J] =
-            fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3])) * scale;
-      }
+    if (l == (J & 63)) keep = mx;
+    if ((J & 63) == 63 || J == I) {
+      wm[(J >> 6) & 1][w][l] = keep;
+      keep = -INFINITY;
     }
   }
+  __syncthreads();
+  store_chunk(I >> 6);
 }
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,

@@ -19,6 +19,7 @@ namespace pxa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -210,6 +211,23 @@ __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// Max over the 64 lanes of a wave without LDS traffic: DPP moves reduce each
+// row of 16 lanes, two row broadcasts fold the rows into lane 63, whose value
+// is returned (wave-uniform).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_move(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL,
+                                                    ROW_MASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_uniform(float x) {
+  x = fmaxf(x, dpp_move<0xB1>(x, x));         // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_move<0x4E>(x, x));         // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_move<0x141>(x, x));        // row_half_mirror
+  x = fmaxf(x, dpp_move<0x140>(x, x));        // row_mirror: every lane holds its row's max
+  x = fmaxf(x, dpp_move<0x142, 0xA>(x, x));   // row_bcast:15 into rows 1 and 3
+  x = fmaxf(x, dpp_move<0x143, 0xC>(x, x));   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -253,6 +271,16 @@ __device__ __forceinline__ int kswz(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int vswz(int row) { return (row & 3) * (D / 32); }
 
+// A wave-uniform pointer moved into scalar registers (64-bit products of
+// uniform values are formed in vector registers and would otherwise stay there).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // One global_load_lds_dwordx4 in scalar-base mode: this lane's 16 bytes at
 // gbase + voff go to LDS byte address lds_wave_base + 16 * lane.  Issued
 // through asm so the compiler does not drain every pending copy before
@@ -265,10 +293,7 @@ __device__ __forceinline__ int vswz(int row) { return (row & 3) * (D / 32); }
 // clobber: it would forbid scalar loads of read-only arguments.
 __device__ __forceinline__ void lds_dma16(const void* gbase_in, uint32_t voff, uint32_t lds_in) {
   // both bases are wave-uniform; readfirstlane puts them in SGPRs
-  const uint64_t gb = (uint64_t)(uintptr_t)gbase_in;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)gb);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(gb >> 32));
-  const void* gbase = (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  const void* gbase = uniform_ptr(gbase_in);
   const uint32_t lds_wave_base = __builtin_amdgcn_readfirstlane(lds_in);
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
@@ -295,7 +320,9 @@ __device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf
   constexpr int ROWS = 64 / C;                // rows per wave instruction
   constexpr int INSTS = kBlock / ROWS / NW;
   static_assert((NW * ROWS) % 16 == 0, "swizzle must repeat every instruction");
-  const int w = (threadIdx.x >> 6) % NW, l = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) % NW;   // scalar
+  const int l = threadIdx.x & 63;
+  g = uniform_ptr(g);
   const int row0 = w * ROWS + l / C;          // row of instruction 0
   const int logical = (l % C) ^ (IS_V ? vswz<D>(row0) : kswz<D>(row0));
   const uint32_t voff = (uint32_t)((l / C) * D + logical * 8) * 2u;   // bytes, same for all it
