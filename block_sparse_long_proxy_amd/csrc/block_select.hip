@@ -12,7 +12,7 @@
 //     is a plain count of blocks ahead of it, so the row lengths (and hence
 //     row_ptr) are known without sorting.
 //   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr, and
-//     a longest-first counting sort of the rows -> row_order.
+//     the XCD-aware, longest-first schedule of the rows -> row_order.
 //   select_emit_kernel : one workgroup per (g, I); bitonic sort of the row's
 //     64-bit (score, index) keys in LDS gives every block's rank; each head
 //     of the group then compacts {J : rank < k or J == I} in ascending J.
@@ -46,16 +46,36 @@ __global__ __launch_bounds__(256) void select_count_kernel(const float* __restri
   }
 }
 
-// Exclusive scan of the n row lengths into row_ptr[0..n]; optionally also a
-// counting sort of the rows by length, longest first, into row_order (the
-// attention kernel's schedule: dispatched round-robin over the XCDs, a
-// longest-first list gives every XCD the same mix of long and short rows).
-// One workgroup; hist needs max_len + 1 ints of dynamic LDS.
+// Exclusive scan of the n row lengths into row_ptr[0..n]; optionally also the
+// attention kernel's schedule row_order.  Workgroup b of a launch goes to XCD
+// b mod 8, and each XCD has its own L2, so the schedule is built per XCD:
+//   * XCD x owns the rows whose midpoint in the cumulative work row_ptr falls
+//     in the x-th eighth.  Rows are numbered h * nb + I and the heads of one
+//     KV head are consecutive, so each XCD sees one or two KV heads and their
+//     K/V tiles stay in its L2;
+//   * position p of row_order is dealt to XCD p mod 8, so XCD x holds exactly
+//     cap_x = ceil-or-floor(n / 8) positions; its own rows fill them longest
+//     first, a surplus (its shortest rows) moves to XCDs with spare positions.
+// The longest-first order P comes from a counting sort by length (rows of
+// equal length in no fixed order) into tmp[n]; stable ranks along P per XCD
+// come from a block-wide scan of eight counters.  One workgroup; hist needs
+// max_len + 1 ints of dynamic LDS.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_of_row(int64_t start, int len, int64_t total) {
+  // midpoint (start + len/2) scaled to [0, 8)
+  const int64_t x = ((2 * start + len) * kXcds) / (2 * total);
+  return (int)min<int64_t>(x, kXcds - 1);
+}
+
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ row_ptr,
                                                                    int32_t* __restrict__ row_order,
+                                                                   int32_t* __restrict__ tmp,
                                                                    int n, int max_len) {
   __shared__ int part[kScanThreads];
+  __shared__ int xc[kScanThreads][kXcds];   // per-thread counts, then exclusive prefixes
+  __shared__ int xtot[kXcds];
   extern __shared__ int hist[];   // [max_len + 1]
   const int t = threadIdx.x;
   const int per = (n + kScanThreads - 1) / kScanThreads;
@@ -79,6 +99,9 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
   }
   if (t == kScanThreads - 1) row_ptr[n] = part[t];
   if (!row_order) return;
+  const int64_t total = part[kScanThreads - 1];
+
+  // P = rows longest first (counting sort)
   for (int i = a; i < b; ++i) atomicAdd(&hist[min(counts[i], max_len)], 1);
   __syncthreads();
   if (t == 0) {   // bucket starts, longest bucket first
@@ -90,7 +113,56 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
     }
   }
   __syncthreads();
-  for (int i = a; i < b; ++i) row_order[atomicAdd(&hist[min(counts[i], max_len)], 1)] = i;
+  for (int i = a; i < b; ++i) tmp[atomicAdd(&hist[min(counts[i], max_len)], 1)] = i;
+  __syncthreads();   // tmp complete: the barrier's fence orders the global writes
+
+  // per-XCD ranks along P: counts of this thread's positions [a, b) of P
+  int mine[kXcds];
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x) mine[x] = 0;
+  for (int p = a; p < b; ++p) {
+    const int r = tmp[p];
+    mine[xcd_of_row(row_ptr[r], counts[r], total)]++;
+  }
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x) xc[t][x] = mine[x];
+  __syncthreads();
+  for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive scan of 8 columns
+    int add[kXcds];
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x) add[x] = t >= off ? xc[t - off][x] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kXcds; ++x) xc[t][x] += add[x];
+    __syncthreads();
+  }
+  if (t < kXcds) xtot[t] = xc[kScanThreads - 1][t];
+  __syncthreads();
+  int cnt[kXcds], cap[kXcds], deficit_start[kXcds + 1];
+  deficit_start[0] = 0;
+#pragma unroll
+  for (int x = 0; x < kXcds; ++x) {
+    cnt[x] = xc[t][x] - mine[x];                       // ranks before this segment
+    cap[x] = n / kXcds + (x < n % kXcds ? 1 : 0);      // positions dealt to XCD x
+    deficit_start[x + 1] = deficit_start[x] + max(0, cap[x] - xtot[x]);
+  }
+  for (int p = a; p < b; ++p) {
+    const int r = tmp[p];
+    const int x = xcd_of_row(row_ptr[r], counts[r], total);
+    int pos;
+    if (cnt[x] < cap[x]) {
+      pos = kXcds * cnt[x] + x;
+    } else {   // surplus: the sj-th surplus row along P takes the sj-th spare position
+      int sj = 0;
+#pragma unroll
+      for (int y = 0; y < kXcds; ++y) sj += max(0, cnt[y] - cap[y]);
+      int y = 0;
+      while (y < kXcds - 1 && sj >= deficit_start[y + 1]) ++y;
+      pos = kXcds * (xtot[y] + (sj - deficit_start[y])) + y;
+    }
+    cnt[x]++;
+    row_order[pos] = r;
+  }
 }
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
@@ -159,8 +231,8 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
   }
 }
 
-size_t select_ws_bytes(const LaunchArgs& a) {
-  return align_up((size_t)a.H * (a.N / kBlock) * sizeof(int32_t), 256);
+size_t select_ws_bytes(const LaunchArgs& a) {   // row lengths + the longest-first order
+  return 2 * align_up((size_t)a.H * (a.N / kBlock) * sizeof(int32_t), 256);
 }
 
 hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
@@ -168,6 +240,7 @@ hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t
                          hipStream_t stream) {
   const int nb = a.N / kBlock;
   int32_t* counts = (int32_t*)ws;
+  int32_t* tmp = (int32_t*)((char*)ws + align_up((size_t)a.H * nb * sizeof(int32_t), 256));
   hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,
                      k_h, counts, a.H, a.G, nb);
   hipError_t e = hipGetLastError();
@@ -175,7 +248,7 @@ hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t
   const int max_len = nb + 1;   // a row keeps at most I + 1 <= nb blocks
   hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads),
                      row_order ? (size_t)(max_len + 1) * sizeof(int) : 0, stream, counts, row_ptr,
-                     row_order, a.H * nb, max_len);
+                     row_order, tmp, a.H * nb, max_len);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int Pmax = 1;

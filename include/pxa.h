@@ -80,7 +80,7 @@ typedef struct pxa_workspace_layout {
   size_t k_h;       /* int32 [H]                         */
   size_t row_ptr;   /* int32 [H*nb + 1]                  */
   size_t col_idx;   /* int32 [H*nb*(nb+1)/2] (capacity)  */
-  size_t row_order; /* int32 [H*nb]: rows longest first  */
+  size_t row_order; /* int32 [H*nb]: attention schedule  */
   size_t budget_ws; /* pxa_budget_workspace_bytes        */
   size_t select_ws; /* pxa_select_workspace_bytes        */
   size_t total;     /* == pxa_workspace_bytes            */
@@ -143,9 +143,14 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k,
  * plus the diagonal block I (k_h < 0 is read as 0).  Output is CSR over rows
  * r = h*nb + I: row_ptr[H*nb+1], col_idx[row_ptr[r] .. row_ptr[r+1])
  * ascending.  col_idx needs pxa_max_col_entries(cfg) capacity.
- * row_order (may be NULL): receives a permutation of the H*nb rows with
- * longer rows first, a schedule for pxa_sparse_prefill (rows of equal length
- * come in no fixed order; it never changes any result).
+ * row_order (may be NULL): receives a permutation of the H*nb rows, the
+ * schedule for pxa_sparse_prefill (it never changes any result).  Position p
+ * is meant for XCD p mod 8 (workgroups are dealt to the 8 XCDs round-robin):
+ * XCD x gets the rows whose midpoint in the cumulative work row_ptr lies in
+ * the x-th eighth (a contiguous range of rows, hence of KV heads, so their
+ * K/V tiles stay in that XCD's L2), longest first; when that is more rows
+ * than it has positions, its shortest rows fill other XCDs' spare positions.
+ * Rows of equal length come in no fixed order.
  * ws: pxa_select_workspace_bytes. */
 int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
                      int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,

@@ -59,6 +59,36 @@ def csr_to_keep(row_ptr: np.ndarray, col_idx: np.ndarray, H: int, nb: int) -> np
     return keep
 
 
+XCDS = 8
+
+
+def check_schedule(order, row_ptr):
+    """Properties of the attention schedule written by the selection stage.
+
+    Position p goes to XCD p mod 8.  XCD x owns the rows whose midpoint in the
+    cumulative work (row_ptr) lies in the x-th eighth; it receives them longest
+    first, as many as it has positions, and its shortest rows beyond that fill
+    the spare positions of other XCDs.
+    """
+    order = np.asarray(order, dtype=np.int64)
+    rp = np.asarray(row_ptr, dtype=np.int64)
+    n = rp.size - 1
+    lens = np.diff(rp)
+    np.testing.assert_array_equal(np.sort(order), np.arange(n))          # a permutation
+    total = rp[-1]
+    owner = np.minimum((2 * rp[:-1] + lens) * XCDS // (2 * total), XCDS - 1)
+    for x in range(XCDS):
+        got = order[x::XCDS]                                              # XCD x's rows in order
+        own = owner[got] == x
+        k = int(np.sum(owner == x))
+        m = min(k, got.size)
+        assert np.all(own[:m]) and not np.any(own[m:]), f"XCD {x}: own rows not first"
+        assert np.all(np.diff(lens[got[:m]]) <= 0), f"XCD {x}: own rows not longest first"
+        moved = np.setdiff1d(np.nonzero(owner == x)[0], got)
+        if moved.size and m:
+            assert lens[moved].max() <= lens[got[:m]].min(), f"XCD {x}: a long row was moved"
+
+
 def cum_at(masses_h: np.ndarray, order: np.ndarray, k: int) -> float:
     return float(np.sum(masses_h[order[:k]], dtype=np.float64))
 
