@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sdpa", action="store_true",
+                    help="skip the context timing of torch's flash SDPA at the same shape")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0,
                     help="approximate CPU seconds for the oracle sample")
     ap.add_argument("--profile", action="store_true",
@@ -115,7 +117,7 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0):
     O.proxy_pool(f64(x["q"][:, :ntok]), f64(x["k"][:, :ntok]), G)
     est["pool"] = (time.perf_counter() - t) * N / ntok
 
-    rows = [nb // 8, nb // 4, nb // 2, (5 * nb) // 8, (3 * nb) // 4, (7 * nb) // 8]
+    rows = sorted({(c * nb) // 16 for c in range(1, 16)})
     qg = f64(x["q"][: H // G])
     kg = f64(x["k"][: max(1, Hkv // G)])
     t = time.perf_counter()
@@ -272,6 +274,29 @@ def main():
     dense_ms = e0.elapsed_time(e1) / a.dense_reps
     log(f"dense: {dense_ms:.3f} ms")
 
+    # context only: torch's own fused causal attention (flash backend) at the same shape,
+    # to show the dense denominator is not a weak baseline
+    sdpa = None
+    if not a.no_sdpa and wl.dtype == "bf16":
+        try:
+            from torch.nn.attention import sdpa_kernel, SDPBackend
+            import torch.nn.functional as F
+            qq, kk, vv = dev["q"][None], dev["k"][None], dev["v"][None]
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                F.scaled_dot_product_attention(qq, kk, vv, is_causal=True, enable_gqa=True)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for _ in range(a.dense_reps):
+                    F.scaled_dot_product_attention(qq, kk, vv, is_causal=True, enable_gqa=True)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            sdpa = {"ms": round(e0.elapsed_time(e1) / a.dense_reps, 3),
+                    "what": "torch.nn.functional.scaled_dot_product_attention, flash backend, "
+                            "is_causal, enable_gqa, same bf16 inputs"}
+            log(f"torch flash SDPA: {sdpa['ms']:.3f} ms")
+        except Exception as e:  # a build without the flash backend: report, do not fail
+            sdpa = {"ms": None, "error": repr(e)[:200]}
+
     # mask statistics
     rp = attn.row_ptr.cpu().numpy().astype(np.int64)
     kh = attn.k_h.cpu().numpy()
@@ -295,8 +320,8 @@ def main():
         ci = attn.col_idx.cpu().numpy()
         rng = np.random.default_rng(7)
         samp = []
-        for h in sorted(rng.choice(H, size=4, replace=False).tolist()):
-            for I in rng.integers(nb // 4, nb, size=3).tolist():
+        for h in sorted(rng.choice(H, size=min(H, 16), replace=False).tolist()):
+            for I in rng.integers(nb // 4, nb, size=16).tolist():
                 r = h * nb + I
                 samp.append((h, I, ci[rp[r]:rp[r + 1]].astype(np.int64)))
         log("timing the CPU oracle on a sample")
@@ -313,6 +338,7 @@ def main():
                    "batch": 1, "input_sha256_16": digest},
         "speedup_vs_dense": round(dense_ms / ms_step, 3),
         "dense_ms": round(dense_ms, 3),
+        "torch_sdpa_dense": sdpa,
         "estimation_ms": round(est_ms, 3),
         "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
         "kept_density": round(density, 4),

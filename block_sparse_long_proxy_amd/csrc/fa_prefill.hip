@@ -77,7 +77,27 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
                                         float scale_log2, int qloc, const __bf16* knext,
                                         const __bf16* vnext) {
   f32x16 s[4];
-  tile_scores<D>(ks_lds, qf, s);
+  // S^T = K Q^T with the four K fragments of k-step ss+1 read while the four
+  // products of step ss issue (scheduling barriers keep that order).
+  {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[t] = zero16();
+    bf16x8 a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = ktile_frag<D>(ks_lds, t, 0);
+#pragma unroll
+    for (int ss = 0; ss < D / 16; ++ss) {
+      bf16x8 an[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) an[t] = (ss + 1 < D / 16) ? ktile_frag<D>(ks_lds, t, ss + 1) : a[t];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s[t] = mfma32(a[t], qf[ss], s[t]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[t] = an[t];
+    }
+  }
   if (DIAG) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
