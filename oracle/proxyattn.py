@@ -11,7 +11,9 @@ it, in the order of its section 4 ("ProxyAttn方法详解"):
   step 1 / Head Pooling       -> proxy_pool
   step 1 / Score Estimation   -> proxy_scores
   step 1 / Block Ranking      -> rank_blocks
-  step 2 / dynamic budget     -> last_block_masses, budget_from_masses
+  step 2 / dynamic budget     -> last_block_masses (last_blocks_masses for a
+                                 probe of several blocks), budget_from_masses
+  budget variants             -> fixed k per head; ratio_count, select_blocks_ratio
   final sparse mask           -> select_blocks
   FlashAttention on the mask  -> sparse_attention
 
@@ -187,6 +189,48 @@ def last_block_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int,
     return P.reshape(block, nb, block).sum(axis=2).mean(axis=0)
 
 
+def last_blocks_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int, scale: float,
+                       m: int) -> np.ndarray:
+    """Mean causal attention mass per key block over the last m query blocks.
+
+    Blog post section 4, step 2 probes "the last small portion" of the query
+    blocks.  Reading for a probe of m >= 1 blocks: the probe set is the last
+    m * B queries; each query's exact softmax over its causal keys; the mass a
+    query puts in key block J is summed over J's keys, then averaged over the
+    whole probe set (so the masses sum to 1).  m = 1 gives last_block_masses.
+
+    q_h: [N, d] one query head, k_kv: [N, d] its KV head -> [nb] float64.
+    """
+    N = q_h.shape[0]
+    nb = N // block
+    if not 1 <= m <= nb:
+        raise ValueError("m must lie in [1, nb]")
+    q64 = np.asarray(q_h, dtype=np.float64)
+    k64 = np.asarray(k_kv, dtype=np.float64)
+    total = np.zeros(nb)
+    for I in range(nb - m, nb):                  # one probe query block at a time
+        rows = np.arange(I * block, (I + 1) * block)
+        L = scale * (q64[rows] @ k64.T)
+        L = np.where(np.arange(N)[None, :] <= rows[:, None], L, NEG_INF)
+        L = L - L.max(axis=1, keepdims=True)
+        P = np.exp(L)
+        P /= P.sum(axis=1, keepdims=True)
+        total += P.reshape(block, nb, block).sum(axis=2).sum(axis=0)
+    return total / (m * block)
+
+
+def ratio_count(I: int, ratio: float) -> int:
+    """Blocks a ratio budget keeps in row I: ceil(r * (I+1)), within [1, I+1].
+
+    The ratio budget is the Top-K-by-proportion choice that the XAttention
+    report (section 2.2) sets against a fixed Top-K and a threshold.  The
+    product is rounded to float32 (nearest-even) before the ceiling: the count
+    is an integer decision, taken in the precision the GPU takes it in.
+    """
+    prod = np.float32(ratio) * np.float32(I + 1)          # float32 x float32 -> float32
+    return int(min(I + 1, max(1, int(np.ceil(prod)))))
+
+
 def budget_from_masses(m: np.ndarray, order: np.ndarray, gamma: float) -> int:
     """k_h: fewest top-ranked blocks whose cumulative mass reaches gamma.
 
@@ -205,11 +249,12 @@ def budget_from_masses(m: np.ndarray, order: np.ndarray, gamma: float) -> int:
 
 
 def budgets(q: np.ndarray, k: np.ndarray, S: np.ndarray, G: int, gamma: float,
-            block: int = 128, scale: Optional[float] = None):
+            block: int = 128, scale: Optional[float] = None, last_blocks: int = 1):
     """k_h for every query head, plus the masses m_h [H, nb].
 
     The ranking used is that of row nb-1 of the head's group (the same ranking
-    the selection applies to that row).
+    the selection applies to that row).  last_blocks > 1 probes the last
+    last_blocks query blocks (last_blocks_masses) instead of the last one.
     """
     H, N, d = q.shape
     Hkv = k.shape[0]
@@ -220,7 +265,9 @@ def budgets(q: np.ndarray, k: np.ndarray, S: np.ndarray, G: int, gamma: float,
     for h in range(H):
         g = group_of(h, H, G)
         order = rank_blocks(S[g, nb - 1], nb - 1)
-        masses[h] = last_block_masses(q[h], k[kv_head_of(h, H, Hkv)], block, scale)
+        kvh = kv_head_of(h, H, Hkv)
+        masses[h] = (last_block_masses(q[h], k[kvh], block, scale) if last_blocks == 1
+                     else last_blocks_masses(q[h], k[kvh], block, scale, last_blocks))
         kh[h] = budget_from_masses(masses[h], order, gamma)
     return kh, masses
 
@@ -234,6 +281,19 @@ def select_row(S_row: np.ndarray, I: int, k: int) -> np.ndarray:
     kept = set(int(J) for J in order[: min(int(k), I + 1)])
     kept.add(I)
     return np.array(sorted(kept), dtype=np.int64)
+
+
+def select_blocks_ratio(S: np.ndarray, ratio: float, H: int,
+                        rows: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Keep mask [H, nb, nb] of the ratio budget: row I keeps the first
+    ratio_count(I, ratio) blocks of its group's ranking plus the diagonal."""
+    G, nb, _ = S.shape
+    keep = np.zeros((H, nb, nb), dtype=bool)
+    for h in range(H):
+        g = group_of(h, H, G)
+        for I in (range(nb) if rows is None else rows):
+            keep[h, I, select_row(S[g, I], I, ratio_count(I, ratio))] = True
+    return keep
 
 
 def select_blocks(S: np.ndarray, kh: Sequence[int], H: int,
@@ -303,8 +363,18 @@ def causal_keep(H: int, nb: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
              block: int = 128, scale: Optional[float] = None,
-             proxies_bf16: bool = True, with_output: bool = True) -> Dict[str, np.ndarray]:
-    """Run every step in order and return all intermediates."""
+             proxies_bf16: bool = True, with_output: bool = True,
+             budget: Optional[Dict] = None) -> Dict[str, np.ndarray]:
+    """Run every step in order and return all intermediates.
+
+    budget (None: the dynamic budget probed on the last query block):
+      {"mode": "dynamic", "last_blocks": m}  dynamic budget probed on m blocks;
+      {"mode": "fixed", "blocks": k}          every head keeps k blocks per row
+                                              (the fixed budget the blog's
+                                              section 4 compares against);
+      {"mode": "ratio", "ratio": r}           row I keeps ratio_count(I, r).
+    """
+    budget = {"mode": "dynamic", "last_blocks": 1} if budget is None else budget
     H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     q = np.asarray(q, dtype=np.float64)
@@ -312,8 +382,18 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
     v = np.asarray(v, dtype=np.float64)
     qbar, kbar = proxy_pool(q, k, G, to_bf16=proxies_bf16)
     S = proxy_scores(qbar, kbar, block, scale)
-    kh, masses = budgets(q, k, S, G, gamma, block, scale)
-    keep = select_blocks(S, kh, H)
+    mode = budget["mode"]
+    if mode == "dynamic":
+        kh, masses = budgets(q, k, S, G, gamma, block, scale, budget.get("last_blocks", 1))
+        keep = select_blocks(S, kh, H)
+    elif mode == "fixed":
+        kh, masses = np.full(H, int(budget["blocks"]), dtype=np.int64), None
+        keep = select_blocks(S, kh, H)
+    elif mode == "ratio":
+        kh, masses = None, None
+        keep = select_blocks_ratio(S, float(budget["ratio"]), H)
+    else:
+        raise ValueError(f"unknown budget mode {mode!r}")
     res = {"qbar": qbar, "kbar": kbar, "S": S, "k_h": kh, "masses": masses, "keep": keep}
     if with_output:
         res["o"] = sparse_attention(q, k, v, keep, block, scale)

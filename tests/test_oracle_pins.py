@@ -319,3 +319,102 @@ def test_heads_use_their_own_groups_scores():
             ref = sorted(range(I + 1), key=lambda J: (-S[g, I, J], J))[: min(2, I + 1)]
             assert list(np.nonzero(keep[h, I])[0]) == sorted(set(ref) | {I})
     assert [O.group_of(h, H, G) for h in range(H)] == [0, 0, 1, 1]
+
+
+# ---------------------------------------------------------------- budget variants
+def _brute_probe_masses(q, k, block, scale, m):
+    """Pure-Python loops over the last m*block queries (math.fsum normaliser)."""
+    N = q.shape[0]
+    nb = N // block
+    out = [0.0] * nb
+    for i in range(N - m * block, N):
+        w = [math.exp(_brute_logit(q[i], k[j], scale)) for j in range(i + 1)]
+        z = math.fsum(w)
+        for j, wj in enumerate(w):
+            out[j // block] += wj / z / (m * block)
+    return np.array(out)
+
+
+def test_probe_masses_of_one_block_equal_the_last_block_masses():
+    q, k = _rand((24, 4), 40, 1.5), _rand((24, 4), 41)
+    np.testing.assert_allclose(O.last_blocks_masses(q, k, 4, 0.7, 1),
+                               O.last_block_masses(q, k, 4, 0.7), rtol=1e-13, atol=1e-16)
+
+
+@pytest.mark.parametrize("m", [2, 3, 6])
+def test_probe_masses_bruteforce_and_sum_to_one(m):
+    q, k = _rand((24, 4), 42, 2.0), _rand((24, 4), 43)
+    got = O.last_blocks_masses(q, k, 4, 0.6, m)
+    np.testing.assert_allclose(got, _brute_probe_masses(q, k, 4, 0.6, m), rtol=1e-12, atol=1e-15)
+    assert got.sum() == pytest.approx(1.0, abs=1e-12)
+
+
+def test_probe_masses_uniform_logits_closed_form():
+    # q = 0: query i spreads 1/(i+1) over keys 0..i, so block J receives
+    # |{j in J : j <= i}| / (i+1); averaged over the probe queries.
+    N, B, m = 32, 8, 3
+    q, k = np.zeros((N, 2)), _rand((N, 2), 44)
+    want = np.zeros(N // B)
+    for i in range(N - m * B, N):
+        for J in range(N // B):
+            cnt = max(0, min(i, (J + 1) * B - 1) - J * B + 1)
+            want[J] += cnt / (i + 1) / (m * B)
+    np.testing.assert_allclose(O.last_blocks_masses(q, k, B, 1.0, m), want, rtol=1e-13, atol=1e-16)
+
+
+def test_probe_masses_library_softmax():
+    N, B, m, d = 64, 8, 4, 4
+    q, k = _rand((N, d), 45, 1.5), _rand((N, d), 46)
+    L = torch.from_numpy(0.5 * q @ k.T)
+    L = L.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+    P = torch.softmax(L, dim=1)[N - m * B:]                     # probe rows
+    want = P.reshape(m * B, N // B, B).sum(dim=2).mean(dim=0).numpy()
+    np.testing.assert_allclose(O.last_blocks_masses(q, k, B, 0.5, m), want, rtol=1e-12, atol=1e-15)
+
+
+def test_ratio_count_rounds_the_product_to_float32():
+    # float32(0.3) * 10 = 3 + 2**-23 exactly, half-way between 3 and the next
+    # float32; nearest-even gives 3.0, so three blocks (float64 would say 4).
+    assert O.ratio_count(9, 0.3) == 3
+    assert math.ceil(float(np.float32(0.3)) * 10) == 4
+    assert O.ratio_count(3, 0.5) == 2
+    assert O.ratio_count(7, 1.0) == 8          # everything causal
+    assert O.ratio_count(1000, 1e-6) == 1      # at least one block
+    assert O.ratio_count(0, 0.2) == 1
+
+
+def test_ratio_selection_bruteforce():
+    rng = np.random.default_rng(47)
+    G, nb, H = 2, 9, 4
+    S = np.where(np.tril(np.ones((nb, nb), dtype=bool)), rng.integers(0, 4, (G, nb, nb)).astype(float), -np.inf)
+    for r in (0.05, 0.3, 0.5, 0.77, 1.0):
+        keep = O.select_blocks_ratio(S, r, H)
+        for h in range(H):
+            g = h // (H // G)
+            for I in range(nb):
+                kk = O.ratio_count(I, r)
+                ranked = sorted(range(I + 1), key=lambda J: (-S[g, I, J], J))
+                want = set(ranked[:kk]) | {I}
+                assert set(np.nonzero(keep[h, I])[0].tolist()) == want
+
+
+def test_pipeline_budget_modes():
+    H, Hkv, N, d, B, G = 4, 2, 32, 4, 4, 2
+    nb = N // B
+    q, k, v = _rand((H, N, d), 48, 0.8), _rand((Hkv, N, d), 49), _rand((Hkv, N, d), 50)
+    dense = _sdpa64(q, k, v, 1 / math.sqrt(d), causal=True)
+    for budget in ({"mode": "fixed", "blocks": nb}, {"mode": "ratio", "ratio": 1.0}):
+        r = O.pipeline(q, k, v, G, 0.5, block=B, budget=budget)
+        assert r["keep"].sum() == H * nb * (nb + 1) // 2
+        np.testing.assert_allclose(r["o"], dense, rtol=1e-12, atol=1e-12)
+    r = O.pipeline(q, k, v, G, 0.5, block=B, budget={"mode": "fixed", "blocks": 1}, with_output=False)
+    assert np.all(r["keep"].sum(axis=2) <= 2) and np.all(r["k_h"] == 1)
+    base = O.pipeline(q, k, v, G, 0.8, block=B, with_output=False)
+    one = O.pipeline(q, k, v, G, 0.8, block=B, with_output=False,
+                     budget={"mode": "dynamic", "last_blocks": 1})
+    np.testing.assert_array_equal(base["keep"], one["keep"])
+    many = O.pipeline(q, k, v, G, 0.8, block=B, with_output=False,
+                      budget={"mode": "dynamic", "last_blocks": 3})
+    for h in range(H):
+        np.testing.assert_allclose(many["masses"][h], O.last_blocks_masses(
+            q[h], k[O.kv_head_of(h, H, Hkv)], B, 1 / math.sqrt(d), 3), rtol=1e-13)
