@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--budget", default="dynamic:1",
+                    help="budget variant: dynamic:M (probe the last M query blocks; the method's "
+                         "own budget, M=1 by default), fixed:K or ratio:R")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true",
                     help="skip the context timing of torch's flash SDPA at the same shape")
@@ -87,7 +90,7 @@ def profiled_traffic(workload):
         return None
 
 
-def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0):
+def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_kind="dynamic"):
     """Time the CPU oracle on a bounded sample and scale it to the full step.
 
     Sample: a token slice of the pooling, three query-block rows of the proxy
@@ -130,11 +133,17 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0):
     est["score"] = (time.perf_counter() - t) * (G * nb * (nb + 1) / 2) / tiles
     del qg, kg
 
-    q0, k0 = f64(x["q"][0]), f64(x["k"][0])
-    t = time.perf_counter()
-    O.last_block_masses(q0, k0, B, scale)
-    est["budget"] = (time.perf_counter() - t) * H
-    del q0, k0
+    if budget_kind == "dynamic":
+        q0, k0 = f64(x["q"][0]), f64(x["k"][0])
+        t = time.perf_counter()
+        if last_blocks == 1:
+            O.last_block_masses(q0, k0, B, scale)
+        else:
+            O.last_blocks_masses(q0, k0, B, scale, last_blocks)
+        est["budget"] = (time.perf_counter() - t) * H
+        del q0, k0
+    else:
+        est["budget"] = 0.0
 
     srow = np.random.default_rng(1).standard_normal(nb)
     t = time.perf_counter()
@@ -190,24 +199,40 @@ def main():
     log(f"generated in {time.time() - t0:.1f}s digest {digest}")
     dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
     torch.cuda.synchronize()
-    attn = pxa.ProxyAttn(cfg)
+    kind, _, val = a.budget.partition(":")
+    budget = {"dynamic": lambda: pxa.Budget.dynamic(int(val or 1)),
+              "fixed": lambda: pxa.Budget.fixed(int(val)),
+              "ratio": lambda: pxa.Budget.ratio_of(float(val))}[kind]()
+    budget_desc = {"mode": kind, **({"last_blocks": budget.last_blocks} if kind == "dynamic" else
+                                    {"blocks": budget.fixed_blocks} if kind == "fixed" else
+                                    {"ratio": budget.ratio})}
+    attn = pxa.ProxyAttn(cfg, budget)
     o = torch.empty_like(dev["q"])
     stream = torch.cuda.current_stream()
+    L = attn.layout
+    bws_bytes = pxa.pxa_budget_workspace_bytes_ex(cfg, budget)
+
+    def budget_stage():
+        if kind != "ratio":
+            pxa.pxa_budget_estimate_ex(cfg, budget, dev["q"], dev["k"], attn.scores, attn.k_h,
+                                       attn.masses, attn.ws[L.budget_ws:], ws_bytes=bws_bytes)
+
+    def select_stage():
+        pxa.pxa_block_select_ex(cfg, budget, attn.scores, None if kind == "ratio" else attn.k_h,
+                                attn.row_ptr, attn.col_idx, attn.ws[L.select_ws:],
+                                ws_bytes=pxa.pxa_select_workspace_bytes(cfg),
+                                row_order=attn.row_order)
 
     if a.profile:
         src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)      # calibration: 256 MiB read + 256 MiB written
         attn(dev["q"], dev["k"], dev["v"], out=o)
-        L = attn.layout
         for _ in range(a.steps):
             pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
             pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
-            pxa.pxa_budget_estimate(cfg, dev["q"], dev["k"], attn.scores, attn.k_h, attn.masses,
-                                    attn.ws[L.budget_ws:], ws_bytes=pxa.pxa_budget_workspace_bytes(cfg))
-            pxa.pxa_block_select(cfg, attn.scores, attn.k_h, attn.row_ptr, attn.col_idx,
-                                 attn.ws[L.select_ws:], ws_bytes=pxa.pxa_select_workspace_bytes(cfg),
-                                 row_order=attn.row_order)
+            budget_stage()
+            select_stage()
             pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
                                    row_order=attn.row_order)
         torch.cuda.synchronize()
@@ -232,10 +257,6 @@ def main():
     log(f"pxa_prefill: {ms_step:.3f} ms/step (host wall {wall_ms:.3f})")
 
     # per-stage timing with the same kernels, events on the launch stream
-    L = attn.layout
-    ws = attn.ws
-    bws = ws[L.budget_ws:]
-    sws = ws[L.select_ws:]
     names = ["pool", "score", "budget", "select", "sparse"]
     acc = {n: 0.0 for n in names}
     reps = max(1, a.steps)
@@ -246,11 +267,9 @@ def main():
         evs[1].record(stream)
         pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
         evs[2].record(stream)
-        pxa.pxa_budget_estimate(cfg, dev["q"], dev["k"], attn.scores, attn.k_h, attn.masses,
-                                bws, ws_bytes=pxa.pxa_budget_workspace_bytes(cfg))
+        budget_stage()
         evs[3].record(stream)
-        pxa.pxa_block_select(cfg, attn.scores, attn.k_h, attn.row_ptr, attn.col_idx, sws,
-                             ws_bytes=pxa.pxa_select_workspace_bytes(cfg), row_order=attn.row_order)
+        select_stage()
         evs[4].record(stream)
         pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
                                row_order=attn.row_order)
@@ -325,7 +344,8 @@ def main():
                 r = h * nb + I
                 samp.append((h, I, ci[rp[r]:rp[r + 1]].astype(np.int64)))
         log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(cfg, x, samp, n_kept, budget_s=a.cpu_budget_s)
+        cpu = cpu_baseline(cfg, x, samp, n_kept, budget_s=a.cpu_budget_s,
+                           last_blocks=budget.last_blocks, budget_kind=kind)
         cpu["value"] = round(cpu["value"], 1)
 
     res = {
@@ -335,14 +355,14 @@ def main():
         "data": "synthetic (seeded generator, bf16, inputs resident in HBM)",
         "config": {"workload": f"{wl.name}: {wl.description}", "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": d, "seq_len": N, "block": B, "num_proxies": G, "gamma": gamma,
-                   "batch": 1, "input_sha256_16": digest},
+                   "batch": 1, "budget": budget_desc, "input_sha256_16": digest},
         "speedup_vs_dense": round(dense_ms / ms_step, 3),
         "dense_ms": round(dense_ms, 3),
         "torch_sdpa_dense": sdpa,
         "estimation_ms": round(est_ms, 3),
         "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
         "kept_density": round(density, 4),
-        "k_h": kh.tolist(),
+        "k_h": kh.tolist() if kind != "ratio" else None,
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "kept_block_mfma_util": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
         "dense_mfma_util": round(tflops(f_dense, dense_ms) / PEAK_BF16_TFLOPS, 4),

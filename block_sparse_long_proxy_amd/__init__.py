@@ -9,6 +9,9 @@ include/pxa.h); this package only marshals torch tensors to it.
     attn = ProxyAttn(cfg)              # allocates the workspace once
     o = attn(q, k, v)                  # q [H,N,d], k/v [Hkv,N,d] bf16 on the GPU
     attn.k_h, attn.row_ptr, attn.col_idx, attn.scores   # the mask it used
+
+Budget variants: ProxyAttn(cfg, Budget.dynamic(last_blocks=4)),
+Budget.fixed(blocks=64), Budget.ratio_of(0.1).
 """
 from ._binding import (  # noqa: F401
     Config, PxaError, load_library, LIB_PATH,
@@ -16,17 +19,21 @@ from ._binding import (  # noqa: F401
     pxa_get_workspace_layout, pxa_budget_workspace_bytes, pxa_select_workspace_bytes,
     pxa_max_col_entries, pxa_prefill, pxa_proxy_pool, pxa_proxy_score, pxa_budget_estimate,
     pxa_block_select, pxa_sparse_prefill, pxa_dense_prefill,
+    Budget, PXA_BUDGET_DYNAMIC, PXA_BUDGET_FIXED, PXA_BUDGET_RATIO, PXA_MAX_PROBE_BLOCKS,
+    pxa_validate_budget, pxa_workspace_bytes_ex, pxa_get_workspace_layout_ex,
+    pxa_budget_workspace_bytes_ex, pxa_prefill_ex, pxa_budget_estimate_ex, pxa_block_select_ex,
 )
 
 
 class ProxyAttn:
     """Whole-pipeline call with a persistent workspace and views of its parts."""
 
-    def __init__(self, cfg: Config, device="cuda"):
+    def __init__(self, cfg: Config, budget: "Budget | None" = None, device="cuda"):
         import torch
         self.cfg = cfg
+        self.budget = budget
         load_library()
-        L = pxa_get_workspace_layout(cfg)
+        L = pxa_get_workspace_layout_ex(cfg, budget)
         self.layout = L
         self.ws = torch.empty(L.total, dtype=torch.uint8, device=device)
         nb, H, G, N, d = cfg.nb, cfg.num_heads, cfg.num_proxies, cfg.seq_len, cfg.head_dim
@@ -47,7 +54,7 @@ class ProxyAttn:
     def __call__(self, q, k, v, out=None, stream=None):
         import torch
         o = out if out is not None else torch.empty_like(q)
-        pxa_prefill(self.cfg, q, k, v, o, self.ws, stream=stream)
+        pxa_prefill_ex(self.cfg, self.budget, q, k, v, o, self.ws, stream=stream)
         return o
 
     def dense(self, q, k, v, out=None, stream=None):

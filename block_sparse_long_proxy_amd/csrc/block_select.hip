@@ -24,10 +24,24 @@ namespace pxa {
 constexpr int kEmitThreads = 256;
 constexpr int kScanThreads = 1024;
 
+// Ranked blocks row I keeps under the ratio budget r: ceil of the float32
+// product r * (I+1) (nearest-even, no contraction), within [1, I+1].  (The
+// Top-K-by-proportion choice of the XAttention report, section 2.2.)
+__device__ __forceinline__ int ratio_count(int I, float r) {
+  const float prod = __fmul_rn(r, (float)(I + 1));
+  return min(I + 1, max(1, (int)ceilf(prod)));
+}
+
+// Budget of row I in head h: the head's k_h, or the ratio budget when k_h is NULL.
+__device__ __forceinline__ int row_budget(const int32_t* __restrict__ k_h, int h, int I,
+                                          float ratio) {
+  return k_h ? max(0, min(k_h[h], I + 1)) : ratio_count(I, ratio);
+}
+
 __global__ __launch_bounds__(256) void select_count_kernel(const float* __restrict__ scores,
                                                            const int32_t* __restrict__ k_h,
                                                            int32_t* __restrict__ counts, int H,
-                                                           int G, int nb) {
+                                                           int G, int nb, float ratio) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // g * nb + I
   const int l = threadIdx.x & 63;
   if (row >= G * nb) return;
@@ -41,7 +55,7 @@ __global__ __launch_bounds__(256) void select_count_kernel(const float* __restri
   const int hpg = H / G;
   for (int hh = l; hh < hpg; hh += 64) {
     const int h = g * hpg + hh;
-    const int kk = max(0, min(k_h[h], I + 1));   // negative budgets: diagonal only
+    const int kk = row_budget(k_h, h, I, ratio);   // negative budgets: diagonal only
     counts[(size_t)h * nb + I] = kk + (ahead >= kk ? 1 : 0);
   }
 }
@@ -168,7 +182,7 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ k_h,
     const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int H, int G, int nb,
-    int Pmax) {
+    int Pmax, float ratio) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);          // [Pmax]
   uint16_t* rank = reinterpret_cast<uint16_t*>(keys + Pmax);   // [nb]
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
   const int wv = t >> 6, ln = t & 63;
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
-    const int kk = max(0, min(k_h[h], n));
+    const int kk = row_budget(k_h, h, I, ratio);
     int c = 0;
     for (int J = a0; J < a1; ++J) c += (rank[J] < kk || J == I) ? 1 : 0;
     // exclusive scan of c over the workgroup
@@ -242,7 +256,7 @@ hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t
   int32_t* counts = (int32_t*)ws;
   int32_t* tmp = (int32_t*)((char*)ws + align_up((size_t)a.H * nb * sizeof(int32_t), 256));
   hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,
-                     k_h, counts, a.H, a.G, nb);
+                     k_h, counts, a.H, a.G, nb, a.ratio);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_len = nb + 1;   // a row keeps at most I + 1 <= nb blocks
@@ -255,7 +269,7 @@ hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t
   while (Pmax < nb) Pmax <<= 1;
   const size_t smem = (size_t)Pmax * 8 + align_up((size_t)nb * 2, 16);
   hipLaunchKernelGGL(select_emit_kernel, dim3(a.G * nb), dim3(kEmitThreads), smem, stream, scores,
-                     k_h, row_ptr, col_idx, a.H, a.G, nb, Pmax);
+                     k_h, row_ptr, col_idx, a.H, a.G, nb, Pmax, a.ratio);
   return hipGetLastError();
 }
 

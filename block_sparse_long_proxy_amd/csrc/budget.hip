@@ -3,18 +3,21 @@
 // ProxyAttn blog post (ir.hit.edu.cn), section 4, step 2: the last small part
 // of the query blocks estimates each head's block-level sparsity, so heads
 // that share one importance ranking get different block budgets.  Reading:
-// the last full query block T (128 queries); each query's exact causal
-// softmax; masses[h][J] = mean over T of the probability mass in key block J;
-// k_h = fewest leading blocks of the group's ranking of row nb-1 (score
-// descending, block ascending on ties) whose masses reach gamma, else nb.
+// the probe is the last m full query blocks (m = 1 by default: 128 queries);
+// each probe query's exact causal softmax; masses[h][J] = mean over the probe
+// queries of the probability mass in key block J; k_h = fewest leading blocks
+// of the group's ranking of row nb-1 (score descending, block ascending on
+// ties) whose masses reach gamma, else nb.  The fixed budget that step is
+// compared with sets k_h to one value for every head (budget_fixed_kernel).
 //
-// Kernel 1 (budget_lse_kernel): one workgroup per (head, run of key blocks);
-//   for each key block J the 128x128 logit tile S^T = K_J Q_T^T (MFMA) is
-//   reduced to a per-query log2-sum-exp2 over that block, lse[h][J][i].
-// Kernel 2 (budget_finalize_kernel): one workgroup per head; merges the
-//   partials into each query's normaliser, forms the block masses, sorts the
-//   last row's scores in LDS (bitonic, 64-bit keys) and scans the masses in
-//   rank order (fp32, fixed chunked order) to find k_h.
+// Kernel 1 (budget_lse_kernel): one workgroup per (head, run of key blocks,
+//   probe block); for each causal key block J the 128x128 logit tile
+//   S^T = K_J Q_T^T (MFMA) is reduced to a per-query log2-sum-exp2 over that
+//   block, lse[h][z][J][i].
+// Kernel 2 (budget_finalize_kernel): one workgroup per head; per probe block,
+//   merges the partials into each query's normaliser and adds the block
+//   masses; then sorts the last row's scores in LDS (bitonic, 64-bit keys)
+//   and scans the masses in rank order (fp32, fixed chunked order) for k_h.
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -26,22 +29,25 @@ constexpr int kFinThreads = 512;
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, float* __restrict__ lse,
-    int H, int Hkv, int N, float scale_log2) {
+    int H, int Hkv, int N, int m, float scale_log2) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
   const int nb = N / kBlock;
   const int h = blockIdx.y;
+  const int z = blockIdx.z;                // probe block z of m
   const int kvh = h / (H / Hkv);
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int qloc = 32 * w + (l & 31);
-  const int I = nb - 1;   // the last query block
+  const int I = nb - m + z;                // its query block
 
+  const int j0 = blockIdx.x * kLseBlocksPerWG;
+  const int j1 = min(I + 1, j0 + kLseBlocksPerWG);   // causal key blocks only
+  if (j0 >= j1) return;
   bf16x8 qf[D / 16];
   load_qfrag<D>(q + ((size_t)h * N + (size_t)I * kBlock + qloc) * D, qf);
   const __bf16* kb = k + (size_t)kvh * N * D;
+  float* out = lse + ((size_t)h * m + z) * nb * kBlock;
 
-  const int j0 = blockIdx.x * kLseBlocksPerWG;
-  const int j1 = min(nb, j0 + kLseBlocksPerWG);
   for (int J = j0; J < j1; ++J) {
     __syncthreads();
     stage_ktile<D>(kb + (size_t)J * kBlock * D, ks);
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) sum += exp2f(fmaf(s[t][r], scale_log2, -mb));
     sum += __shfl_xor(sum, 32, 64);
-    if (l < 32) lse[((size_t)h * nb + J) * kBlock + qloc] = mb + log2f(sum);
+    if (l < 32) out[(size_t)J * kBlock + qloc] = mb + log2f(sum);
   }
 }
 
@@ -93,11 +99,11 @@ __device__ __forceinline__ void bitonic_sort_u64(uint64_t* keys, int P) {
 
 __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
     const float* __restrict__ lse, const float* __restrict__ scores, int32_t* __restrict__ k_h,
-    float* __restrict__ masses, int H, int G, int nb, int P, float gamma) {
+    float* __restrict__ masses, int H, int G, int nb, int m, int P, float gamma) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);              // [P]
-  float* m = reinterpret_cast<float*>(keys + P);                    // [nb]
-  float* qlse = m + nb;                                             // [128]
+  float* mass = reinterpret_cast<float*>(keys + P);                 // [nb]
+  float* qlse = mass + nb;                                          // [128]
   float* part_l = qlse + kBlock;                                    // [4][128]
   float* part_s = part_l + 4 * kBlock;                              // [4][128]
   float* csum = part_s + 4 * kBlock;                                // [kFinThreads]
@@ -106,54 +112,62 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
   const int h = blockIdx.x;
   const int g = h / (H / G);
   const int t = threadIdx.x;
-  const float* L = lse + (size_t)h * nb * kBlock;
 
-  // 1. per-query normaliser (log2 domain), 4 partial merges per query.
-  {
-    const int i = t % kBlock, part = t / kBlock;   // kFinThreads == 4 * 128
-    float mx = -INFINITY, sm = 0.f;
-    for (int J = part; J < nb; J += 4) {
-      const float x = L[(size_t)J * kBlock + i];
-      if (x > mx) {
-        sm = sm * exp2f(mx - x) + 1.f;
-        mx = x;
-      } else {
-        sm += exp2f(x - mx);
-      }
-    }
-    part_l[part * kBlock + i] = mx;
-    part_s[part * kBlock + i] = sm;
-  }
-  // 3a. sort keys of the group's last row (load while the partials settle).
+  // 3a. sort keys of the group's last row (loaded first, sorted below).
   const float* srow = scores + ((size_t)g * nb + (nb - 1)) * nb;
   for (int J = t; J < P; J += kFinThreads)
     keys[J] = J < nb ? rank_key(srow[J], (uint32_t)J) : ~0ull;
+  for (int J = t; J < nb; J += kFinThreads) mass[J] = 0.f;
   if (t == 0) first_hit = nb;
-  __syncthreads();
-  if (t < kBlock) {
-    float mx = -INFINITY;
-    for (int p = 0; p < 4; ++p) mx = fmaxf(mx, part_l[p * kBlock + t]);
-    float sm = 0.f;
-    for (int p = 0; p < 4; ++p) {
-      const float lp = part_l[p * kBlock + t];
-      if (lp != -INFINITY) sm += part_s[p * kBlock + t] * exp2f(lp - mx);
-    }
-    qlse[t] = mx + log2f(sm);
-  }
-  __syncthreads();
 
-  // 2. block masses: one wave per block J, lanes over the 128 queries.
-  {
-    const int wv = t >> 6, ln = t & 63, nw = kFinThreads / 64;
-    for (int J = wv; J < nb; J += nw) {
-      const float* r = L + (size_t)J * kBlock;
-      float v = exp2f(r[ln] - qlse[ln]) + exp2f(r[ln + 64] - qlse[ln + 64]);
-      v = wave_sum(v);
-      if (ln == 0) {
-        const float mJ = v * (1.0f / kBlock);
-        m[J] = mJ;
-        masses[(size_t)h * nb + J] = mJ;
+  for (int z = 0; z < m; ++z) {            // probe blocks, in order
+    const int I = nb - m + z;              // causal key blocks 0..I
+    const float* L = lse + ((size_t)h * m + z) * nb * kBlock;
+    // 1. per-query normaliser (log2 domain), 4 partial merges per query.
+    {
+      const int i = t % kBlock, part = t / kBlock;   // kFinThreads == 4 * 128
+      float mx = -INFINITY, sm = 0.f;
+      for (int J = part; J <= I; J += 4) {
+        const float x = L[(size_t)J * kBlock + i];
+        if (x > mx) {
+          sm = sm * exp2f(mx - x) + 1.f;
+          mx = x;
+        } else {
+          sm += exp2f(x - mx);
+        }
       }
+      part_l[part * kBlock + i] = mx;
+      part_s[part * kBlock + i] = sm;
+    }
+    __syncthreads();
+    if (t < kBlock) {
+      float mx = -INFINITY;
+      for (int p = 0; p < 4; ++p) mx = fmaxf(mx, part_l[p * kBlock + t]);
+      float sm = 0.f;
+      for (int p = 0; p < 4; ++p) {
+        const float lp = part_l[p * kBlock + t];
+        if (lp != -INFINITY) sm += part_s[p * kBlock + t] * exp2f(lp - mx);
+      }
+      qlse[t] = mx + log2f(sm);
+    }
+    __syncthreads();
+    // 2. block masses: one wave per block J, lanes over the 128 queries.
+    {
+      const int wv = t >> 6, ln = t & 63, nw = kFinThreads / 64;
+      for (int J = wv; J <= I; J += nw) {
+        const float* r = L + (size_t)J * kBlock;
+        float v = exp2f(r[ln] - qlse[ln]) + exp2f(r[ln + 64] - qlse[ln + 64]);
+        v = wave_sum(v);
+        if (ln == 0) mass[J] += v;
+      }
+    }
+    __syncthreads();   // qlse / part arrays are reused by the next probe block
+  }
+  {
+    const float inv = 1.0f / (float)(m * kBlock);
+    for (int J = t; J < nb; J += kFinThreads) {
+      mass[J] *= inv;
+      masses[(size_t)h * nb + J] = mass[J];
     }
   }
   // 3b. ranking of row nb-1.
@@ -163,7 +177,7 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
   const int per = (nb + kFinThreads - 1) / kFinThreads;
   const int r0 = min(nb, t * per), r1 = min(nb, r0 + per);
   float own = 0.f;
-  for (int r = r0; r < r1; ++r) own += m[(uint32_t)keys[r]];
+  for (int r = r0; r < r1; ++r) own += mass[(uint32_t)keys[r]];
   csum[t] = own;
   __syncthreads();
   if (t == 0) {   // exclusive scan of the chunk sums (sequential, fixed order)
@@ -177,7 +191,7 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
   __syncthreads();
   float cum = csum[t];
   for (int r = r0; r < r1; ++r) {
-    cum += m[(uint32_t)keys[r]];
+    cum += mass[(uint32_t)keys[r]];
     if (cum >= gamma) {
       atomicMin(&first_hit, r);
       break;
@@ -193,8 +207,20 @@ static int pow2_at_least(int n) {
   return p;
 }
 
-size_t budget_ws_bytes(const LaunchArgs& a) {
-  return align_up((size_t)a.H * (a.N / kBlock) * kBlock * sizeof(float), 256);
+size_t budget_ws_bytes(const LaunchArgs& a) {   // lse [H][m][nb][128]
+  const size_t m = a.budget_mode == kBudgetDynamic ? (size_t)a.last_blocks : 1;
+  return align_up((size_t)a.H * m * (a.N / kBlock) * kBlock * sizeof(float), 256);
+}
+
+__global__ void budget_fixed_kernel(int32_t* __restrict__ k_h, int H, int k) {
+  for (int h = blockIdx.x * blockDim.x + threadIdx.x; h < H; h += gridDim.x * blockDim.x)
+    k_h[h] = k;
+}
+
+hipError_t launch_fixed_budget(const LaunchArgs& a, int32_t* k_h, hipStream_t stream) {
+  hipLaunchKernelGGL(budget_fixed_kernel, dim3((a.H + 255) / 256), dim3(256), 0, stream, k_h, a.H,
+                     a.fixed_blocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, const float* scores,
@@ -202,19 +228,20 @@ hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, cons
   const int nb = a.N / kBlock;
   float* lse = (float*)ws;
   const float sl2 = a.scale * kLog2e;
-  const dim3 g1((nb + kLseBlocksPerWG - 1) / kLseBlocksPerWG, a.H);
+  const int m = a.last_blocks;
+  const dim3 g1((nb + kLseBlocksPerWG - 1) / kLseBlocksPerWG, a.H, m);
   if (a.D == 64)
     hipLaunchKernelGGL(budget_lse_kernel<64>, g1, dim3(kThreads), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, sl2);
+                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, m, sl2);
   else
     hipLaunchKernelGGL(budget_lse_kernel<128>, g1, dim3(kThreads), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, sl2);
+                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, m, sl2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = pow2_at_least(nb);
   const size_t smem = (size_t)P * 8 + (size_t)nb * 4 + (size_t)kBlock * 4 * 9 + kFinThreads * 4;
   hipLaunchKernelGGL(budget_finalize_kernel, dim3(a.H), dim3(kFinThreads), smem, stream, lse,
-                     scores, k_h, masses, a.H, a.G, nb, P, a.gamma);
+                     scores, k_h, masses, a.H, a.G, nb, m, P, a.gamma);
   return hipGetLastError();
 }
 

@@ -39,7 +39,30 @@ int check_config(const pxa_config* c) {
   return PXA_OK;
 }
 
-pxa::LaunchArgs args_of(const pxa_config* c) {
+// Budget variant check against a valid configuration; NULL is the default.
+int check_budget(const pxa_config* c, const pxa_budget* b) {
+  if (!b) return PXA_OK;
+  const int nb = c->seq_len / pxa::kBlockTokens;
+  switch (b->mode) {
+    case PXA_BUDGET_DYNAMIC:
+      if (b->last_blocks < 1 || b->last_blocks > nb || b->last_blocks > PXA_MAX_PROBE_BLOCKS)
+        return PXA_EINVAL;
+      return PXA_OK;
+    case PXA_BUDGET_FIXED:
+      return b->fixed_blocks >= 1 ? PXA_OK : PXA_EINVAL;
+    case PXA_BUDGET_RATIO:
+      return (std::isfinite(b->ratio) && b->ratio > 0.f && b->ratio <= 1.f) ? PXA_OK : PXA_EINVAL;
+    default:
+      return PXA_EINVAL;
+  }
+}
+
+int check_all(const pxa_config* c, const pxa_budget* b) {
+  const int rc = check_config(c);
+  return rc != PXA_OK ? rc : check_budget(c, b);
+}
+
+pxa::LaunchArgs args_of(const pxa_config* c, const pxa_budget* b = nullptr) {
   pxa::LaunchArgs a;
   a.H = c->num_heads;
   a.Hkv = c->num_kv_heads;
@@ -48,6 +71,12 @@ pxa::LaunchArgs args_of(const pxa_config* c) {
   a.G = c->num_proxies;
   a.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
   a.gamma = c->gamma;
+  if (b) {
+    a.budget_mode = b->mode;
+    a.last_blocks = b->mode == PXA_BUDGET_DYNAMIC ? b->last_blocks : 1;
+    a.fixed_blocks = b->fixed_blocks;
+    a.ratio = b->ratio;
+  }
   return a;
 }
 
@@ -77,8 +106,8 @@ int hip_rc(hipError_t e) {
   return PXA_EHIP;
 }
 
-void layout_of(const pxa_config* c, pxa_workspace_layout* L) {
-  const pxa::LaunchArgs a = args_of(c);
+void layout_of(const pxa_config* c, const pxa_budget* b, pxa_workspace_layout* L) {
+  const pxa::LaunchArgs a = args_of(c, b);
   const size_t nb = (size_t)a.N / pxa::kBlockTokens;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -108,7 +137,7 @@ int pxa_abi_version(void) { return PXA_ABI_VERSION; }
 const char* pxa_strerror(int code) {
   switch (code) {
     case PXA_OK: return "ok";
-    case PXA_EINVAL: return "invalid configuration (shape, grouping, gamma or scale)";
+    case PXA_EINVAL: return "invalid configuration (shape, grouping, gamma, scale or budget)";
     case PXA_EUNSUPPORTED: return "unsupported configuration (head_dim, block, seq_len)";
     case PXA_ENULL: return "null pointer";
     case PXA_EALIGN: return "misaligned pointer";
@@ -125,7 +154,7 @@ int pxa_validate_config(const pxa_config* cfg) { return check_config(cfg); }
 size_t pxa_workspace_bytes(const pxa_config* cfg) {
   if (check_config(cfg) != PXA_OK) return 0;
   pxa_workspace_layout L;
-  layout_of(cfg, &L);
+  layout_of(cfg, nullptr, &L);
   return L.total;
 }
 
@@ -133,7 +162,7 @@ int pxa_get_workspace_layout(const pxa_config* cfg, pxa_workspace_layout* out) {
   const int rc = check_config(cfg);
   if (rc != PXA_OK) return rc;
   if (!out) return PXA_ENULL;
-  layout_of(cfg, out);
+  layout_of(cfg, nullptr, out);
   return PXA_OK;
 }
 
@@ -153,6 +182,31 @@ size_t pxa_max_col_entries(const pxa_config* cfg) {
   return (size_t)cfg->num_heads * nb * (nb + 1) / 2;
 }
 
+int pxa_validate_budget(const pxa_config* cfg, const pxa_budget* budget) {
+  return check_all(cfg, budget);
+}
+
+size_t pxa_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget) {
+  if (check_all(cfg, budget) != PXA_OK) return 0;
+  pxa_workspace_layout L;
+  layout_of(cfg, budget, &L);
+  return L.total;
+}
+
+int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_budget* budget,
+                                pxa_workspace_layout* out) {
+  const int rc = check_all(cfg, budget);
+  if (rc != PXA_OK) return rc;
+  if (!out) return PXA_ENULL;
+  layout_of(cfg, budget, out);
+  return PXA_OK;
+}
+
+size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget) {
+  if (check_all(cfg, budget) != PXA_OK) return 0;
+  return pxa::budget_ws_bytes(args_of(cfg, budget));
+}
+
 int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k, void* qbar, void* kbar,
                    void* stream) {
   int rc = check_config(cfg);
@@ -169,27 +223,47 @@ int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar, f
   return hip_rc(pxa::launch_proxy_score(args_of(cfg), qbar, kbar, scores, (hipStream_t)stream));
 }
 
-int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k, const float* scores,
-                        int32_t* k_h, float* masses, void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_config(cfg);
+int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+                           const void* k, const float* scores, int32_t* k_h, float* masses,
+                           void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_all(cfg, budget);
   if (rc) return rc;
+  const pxa::LaunchArgs a = args_of(cfg, budget);
+  if (a.budget_mode == pxa::kBudgetRatio) return PXA_EINVAL;   // no per-head budget
+  if (a.budget_mode == pxa::kBudgetFixed) {
+    if ((rc = ptrs_ok({{k_h, 4}}))) return rc;
+    return hip_rc(pxa::launch_fixed_budget(a, k_h, (hipStream_t)stream));
+  }
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {scores, 4}, {k_h, 4}, {masses, 4}, {ws, 256}}))) return rc;
-  const pxa::LaunchArgs a = args_of(cfg);
   if (ws_bytes < pxa::budget_ws_bytes(a)) return PXA_EWORKSPACE;
   return hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, ws, (hipStream_t)stream));
+}
+
+int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k, const float* scores,
+                        int32_t* k_h, float* masses, void* ws, size_t ws_bytes, void* stream) {
+  return pxa_budget_estimate_ex(cfg, nullptr, q, k, scores, k_h, masses, ws, ws_bytes, stream);
+}
+
+int pxa_block_select_ex(const pxa_config* cfg, const pxa_budget* budget, const float* scores,
+                        const int32_t* k_h, int32_t* row_ptr, int32_t* col_idx,
+                        int32_t* row_order, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_all(cfg, budget);
+  if (rc) return rc;
+  const pxa::LaunchArgs a = args_of(cfg, budget);
+  const bool ratio = a.budget_mode == pxa::kBudgetRatio;
+  if ((rc = ptrs_ok({{scores, 4}, {row_ptr, 4}, {col_idx, 4}, {ws, 256}}))) return rc;
+  if (!ratio && (rc = ptrs_ok({{k_h, 4}}))) return rc;
+  if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
+  if (ws_bytes < pxa::select_ws_bytes(a)) return PXA_EWORKSPACE;
+  return hip_rc(pxa::launch_select(a, scores, ratio ? nullptr : k_h, row_ptr, col_idx, row_order,
+                                   ws, (hipStream_t)stream));
 }
 
 int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
                      int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
                      size_t ws_bytes, void* stream) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if ((rc = ptrs_ok({{scores, 4}, {k_h, 4}, {row_ptr, 4}, {col_idx, 4}, {ws, 256}}))) return rc;
-  if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
-  const pxa::LaunchArgs a = args_of(cfg);
-  if (ws_bytes < pxa::select_ws_bytes(a)) return PXA_EWORKSPACE;
-  return hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, row_order, ws,
-                                   (hipStream_t)stream));
+  return pxa_block_select_ex(cfg, nullptr, scores, k_h, row_ptr, col_idx, row_order, ws, ws_bytes,
+                             stream);
 }
 
 int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
@@ -212,15 +286,16 @@ int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const
                                        true, (hipStream_t)stream));
 }
 
-int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
-                void* ws, size_t ws_bytes, void* stream) {
-  int rc = check_config(cfg);
+int pxa_prefill_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+                   const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
+                   void* stream) {
+  int rc = check_all(cfg, budget);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}, {ws, 256}}))) return rc;
   pxa_workspace_layout L;
-  layout_of(cfg, &L);
+  layout_of(cfg, budget, &L);
   if (ws_bytes < L.total) return PXA_EWORKSPACE;
-  const pxa::LaunchArgs a = args_of(cfg);
+  const pxa::LaunchArgs a = args_of(cfg, budget);
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   void* qbar = w + L.qbar;
@@ -233,11 +308,21 @@ int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void*
   int32_t* row_order = (int32_t*)(w + L.row_order);
   if ((rc = hip_rc(pxa::launch_proxy_pool(a, q, k, qbar, kbar, s)))) return rc;
   if ((rc = hip_rc(pxa::launch_proxy_score(a, qbar, kbar, scores, s)))) return rc;
-  if ((rc = hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, w + L.budget_ws, s)))) return rc;
-  if ((rc = hip_rc(pxa::launch_select(a, scores, k_h, row_ptr, col_idx, row_order,
-                                      w + L.select_ws, s))))
+  if (a.budget_mode == pxa::kBudgetDynamic)
+    rc = hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, w + L.budget_ws, s));
+  else if (a.budget_mode == pxa::kBudgetFixed)
+    rc = hip_rc(pxa::launch_fixed_budget(a, k_h, s));
+  if (rc) return rc;
+  const bool ratio = a.budget_mode == pxa::kBudgetRatio;
+  if ((rc = hip_rc(pxa::launch_select(a, scores, ratio ? nullptr : k_h, row_ptr, col_idx,
+                                      row_order, w + L.select_ws, s))))
     return rc;
   return hip_rc(pxa::launch_fa_prefill(a, q, k, v, row_ptr, col_idx, row_order, o, false, s));
+}
+
+int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
+                void* ws, size_t ws_bytes, void* stream) {
+  return pxa_prefill_ex(cfg, nullptr, q, k, v, o, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

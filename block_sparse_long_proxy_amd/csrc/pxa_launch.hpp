@@ -9,10 +9,16 @@ namespace pxa {
 
 constexpr int kBlockTokens = 128;   // block edge the kernels are built for
 
+enum BudgetMode { kBudgetDynamic = 0, kBudgetFixed = 1, kBudgetRatio = 2 };
+
 struct LaunchArgs {
   int H, Hkv, N, D, G;
   float scale;   // softmax scale (already defaulted)
   float gamma;
+  int budget_mode = kBudgetDynamic;
+  int last_blocks = 1;    // dynamic budget: query blocks probed
+  int fixed_blocks = 0;   // fixed budget: blocks per row
+  float ratio = 0.f;      // ratio budget
 };
 
 hipError_t launch_proxy_pool(const LaunchArgs& a, const void* q, const void* k, void* qbar,
@@ -23,8 +29,11 @@ hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void*
 size_t budget_ws_bytes(const LaunchArgs& a);
 hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, const float* scores,
                          int32_t* k_h, float* masses, void* ws, hipStream_t stream);
+// fixed budget: k_h[h] = a.fixed_blocks
+hipError_t launch_fixed_budget(const LaunchArgs& a, int32_t* k_h, hipStream_t stream);
 // ws: select_ws_bytes(a) bytes
 size_t select_ws_bytes(const LaunchArgs& a);
+// k_h NULL: the ratio budget a.ratio
 hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
                          hipStream_t stream);

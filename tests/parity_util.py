@@ -101,34 +101,42 @@ def budget_allowed(masses_h, order, k_gpu, k_ref, gamma) -> bool:
     return all(abs(cum_at(masses_h, order, k) - gamma) < GAMMA_WINDOW for k in range(lo, hi))
 
 
-def compare_masks(keep_gpu, S_ref, kh_ref, kh_gpu, masses_ref, G, gamma, rows=None):
-    """Apply the end-to-end mask rule; return (agree_fraction, report dict)."""
+def compare_masks(keep_gpu, S_ref, kh_ref, kh_gpu, masses_ref, G, gamma, rows=None,
+                  row_k=None):
+    """Apply the end-to-end mask rule; return (agree_fraction, report dict).
+
+    row_k(h, I), when given, is the budget of row I (fixed and ratio budgets:
+    the same on both sides, so only score gaps at the cut may differ)."""
     H, nb, _ = keep_gpu.shape
     rows = range(nb) if rows is None else list(rows)
     total = same = gap_ok = 0
     bad = []
     head_ok = {}
     for h in range(H):
+        if row_k is not None:
+            head_ok[h] = True
+            continue
         g = O.group_of(h, H, G)
         order_last = O.rank_blocks(S_ref[g, nb - 1], nb - 1)
         head_ok[h] = budget_allowed(masses_ref[h], order_last, int(kh_gpu[h]), int(kh_ref[h]), gamma)
     for h in range(H):
         g = O.group_of(h, H, G)
         for I in rows:
+            kI = row_k(h, I) if row_k is not None else kh_ref[h]
             ref = np.zeros(nb, dtype=bool)
-            ref[O.select_row(S_ref[g, I], I, kh_ref[h])] = True
+            ref[O.select_row(S_ref[g, I], I, kI)] = True
             got = keep_gpu[h, I]
             total += I + 1
             diff = np.nonzero(ref[: I + 1] != got[: I + 1])[0]
             same += I + 1 - diff.size
             if diff.size == 0:
                 continue
-            if kh_gpu[h] != kh_ref[h] and head_ok[h]:
+            if row_k is None and kh_gpu[h] != kh_ref[h] and head_ok[h]:
                 gap_ok += diff.size
                 continue
             order = O.rank_blocks(S_ref[g, I], I)
             s = np.asarray(S_ref[g, I], dtype=np.float32).astype(np.float64)
-            k = min(int(kh_ref[h]), I + 1)
+            k = min(int(kI), I + 1)
             cut = [s[order[c]] for c in (k - 1, k) if 0 <= c <= I]
             for J in diff:
                 rel = min(abs(s[J] - c) / max(abs(s[J]), abs(c), 1e-30) for c in cut)

@@ -1,0 +1,74 @@
+"""Budget variants at a full workload size (32K tokens, one proxy), run as the
+benchmark runs them (pxa_prefill_ex): the probe masses of every head against
+the oracle, and the size-independent properties of each variant's mask."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import block_sparse_long_proxy_amd as pxa  # noqa: E402
+from oracle import proxyattn as O  # noqa: E402
+from synth import get_config, generate, bf16_bits_to_f32  # noqa: E402
+from parity_util import budget_allowed, check_schedule, MASS_ATOL, MASS_RTOL  # noqa: E402
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
+
+
+@pytest.fixture(scope="module")
+def data():
+    wl = get_config("c1")
+    print(f"[fullsize-budget] generating {wl.name} N={wl.seq_len}", flush=True)
+    x = generate(wl)
+    cfg = pxa.Config(wl.num_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.num_proxies, wl.gamma)
+    dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
+    return wl, cfg, x, dev
+
+
+def _run(cfg, dev, budget):
+    attn = pxa.ProxyAttn(cfg, budget)
+    attn(dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    rp = attn.row_ptr.cpu().numpy()
+    return attn, rp, attn.col_idx[: int(rp[-1])].cpu().numpy()
+
+
+def test_probe_of_four_blocks(data):
+    wl, cfg, x, dev = data
+    m = 4
+    attn, rp, ci = _run(cfg, dev, pxa.Budget.dynamic(m))
+    H, Hkv, G, nb = cfg.num_heads, cfg.num_kv_heads, cfg.num_proxies, cfg.nb
+    S = attn.scores.cpu().numpy().astype(np.float64)
+    masses, kh = attn.masses.cpu().numpy().astype(np.float64), attn.k_h.cpu().numpy()
+    f64 = lambda a: bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    for h in range(0, H, 3):
+        ref = O.last_blocks_masses(f64(x["q"][h]), f64(x["k"][O.kv_head_of(h, H, Hkv)]), 128,
+                                   cfg.scale, m)
+        assert np.all(np.abs(masses[h] - ref) <= MASS_ATOL + MASS_RTOL * ref), h
+        order = O.rank_blocks(S[O.group_of(h, H, G), nb - 1], nb - 1)
+        assert budget_allowed(ref, order, int(kh[h]), O.budget_from_masses(ref, order, wl.gamma),
+                              wl.gamma), h
+    lens = np.diff(rp).reshape(H, nb)
+    kk = np.minimum(kh[:, None], np.arange(nb)[None, :] + 1)
+    assert np.all((lens == kk) | (lens == kk + 1))
+    check_schedule(attn.row_order.cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("budget,count", [
+    (pxa.Budget.fixed(16), lambda I: min(16, I + 1)),
+    (pxa.Budget.ratio_of(0.1), lambda I: O.ratio_count(I, 0.1)),
+], ids=["fixed16", "ratio0.1"])
+def test_fixed_and_ratio_masks(data, budget, count):
+    wl, cfg, x, dev = data
+    attn, rp, ci = _run(cfg, dev, budget)
+    H, G, nb = cfg.num_heads, cfg.num_proxies, cfg.nb
+    lens = np.diff(rp).reshape(H, nb)
+    kk = np.array([count(I) for I in range(nb)])[None, :]
+    assert np.all((lens == kk) | (lens == kk + 1))
+    S = attn.scores.cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(5)
+    for h in sorted(rng.choice(H, size=4, replace=False).tolist()):
+        for I in sorted({0, nb - 1, *rng.integers(0, nb, size=6).tolist()}):
+            r = h * nb + I
+            want = O.select_row(S[O.group_of(h, H, G), I], I, count(I))
+            np.testing.assert_array_equal(ci[rp[r]:rp[r + 1]], want)
+    check_schedule(attn.row_order.cpu().numpy(), rp)
