@@ -9,7 +9,8 @@ the ProxyAttn blog post (ir.hit.edu.cn, "ProxyAttn ... ICLR 2026") describes
 it, in the order of its section 4 ("ProxyAttn方法详解"):
 
   step 1 / Head Pooling       -> proxy_pool
-  step 1 / Score Estimation   -> proxy_scores
+  step 1 / Score Estimation   -> proxy_scores (query_stride: the sequence-level
+                                 skip of section 5, an approximation)
   step 1 / Block Ranking      -> rank_blocks
   step 2 / dynamic budget     -> last_block_masses (last_blocks_masses for a
                                  probe of several blocks), budget_from_masses
@@ -118,26 +119,35 @@ def proxy_pool(q: np.ndarray, k: np.ndarray, G: int, to_bf16: bool = True):
 # step 1: score estimation (token-level logits, block max-pool)
 # --------------------------------------------------------------------------
 def proxy_score_row(qbar_g: np.ndarray, kbar_g: np.ndarray, I: int, block: int,
-                    scale: float) -> np.ndarray:
+                    scale: float, query_stride: int = 1) -> np.ndarray:
     """Block scores of query-block row I for one proxy: float64 [I+1].
 
     Blog post section 4, step 1 "Score Estimation": token-level proxy scores,
     then a block-level max pool (section 2 fixes the 128x128 block).  Causal
     prefill: inside the diagonal block only keys j <= i count.
+
+    query_stride s > 1 is the sequence-level skip that section 5 credits for
+    the low estimation cost, in this reading: only every s-th query of the
+    block is scored, the queries at offsets s-1, 2s-1, ..., B-1 (the block's
+    last query, which sees the whole diagonal block, is always one of them);
+    every key is kept.  An approximation of the s = 1 score (never larger).
     """
-    rows = slice(I * block, (I + 1) * block)
-    L = scale * (qbar_g[rows] @ kbar_g[: (I + 1) * block].T)      # [B, (I+1)B]
-    i_idx = np.arange(I * block, (I + 1) * block)[:, None]
+    if query_stride < 1 or block % query_stride:
+        raise ValueError("query_stride must divide the block")
+    rows = np.arange(I * block + query_stride - 1, (I + 1) * block, query_stride)
+    L = scale * (qbar_g[rows] @ kbar_g[: (I + 1) * block].T)      # [B/s, (I+1)B]
     j_idx = np.arange((I + 1) * block)[None, :]
-    L = np.where(j_idx <= i_idx, L, NEG_INF)
-    return L.reshape(block, I + 1, block).max(axis=(0, 2))
+    L = np.where(j_idx <= rows[:, None], L, NEG_INF)
+    return L.reshape(rows.size, I + 1, block).max(axis=(0, 2))
 
 
 def proxy_scores(qbar: np.ndarray, kbar: np.ndarray, block: int = 128,
-                 scale: Optional[float] = None, rows: Optional[Iterable[int]] = None) -> np.ndarray:
+                 scale: Optional[float] = None, rows: Optional[Iterable[int]] = None,
+                 query_stride: int = 1) -> np.ndarray:
     """S[g, I, J] for all proxies: float64 [G, nb, nb], -inf above the diagonal.
 
     rows: optional subset of query-block rows to fill (others stay -inf).
+    query_stride: see proxy_score_row.
     """
     G, N, d = qbar.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -145,7 +155,7 @@ def proxy_scores(qbar: np.ndarray, kbar: np.ndarray, block: int = 128,
     S = np.full((G, nb, nb), NEG_INF)
     for g in range(G):
         for I in (range(nb) if rows is None else rows):
-            S[g, I, : I + 1] = proxy_score_row(qbar[g], kbar[g], I, block, scale)
+            S[g, I, : I + 1] = proxy_score_row(qbar[g], kbar[g], I, block, scale, query_stride)
     return S
 
 
@@ -364,7 +374,7 @@ def causal_keep(H: int, nb: int) -> np.ndarray:
 def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
              block: int = 128, scale: Optional[float] = None,
              proxies_bf16: bool = True, with_output: bool = True,
-             budget: Optional[Dict] = None) -> Dict[str, np.ndarray]:
+             budget: Optional[Dict] = None, score_stride: int = 1) -> Dict[str, np.ndarray]:
     """Run every step in order and return all intermediates.
 
     budget (None: the dynamic budget probed on the last query block):
@@ -373,6 +383,7 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
                                               (the fixed budget the blog's
                                               section 4 compares against);
       {"mode": "ratio", "ratio": r}           row I keeps ratio_count(I, r).
+    score_stride: the sequence-level skip of the scoring (proxy_score_row).
     """
     budget = {"mode": "dynamic", "last_blocks": 1} if budget is None else budget
     H, N, d = q.shape
@@ -381,7 +392,7 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     qbar, kbar = proxy_pool(q, k, G, to_bf16=proxies_bf16)
-    S = proxy_scores(qbar, kbar, block, scale)
+    S = proxy_scores(qbar, kbar, block, scale, query_stride=score_stride)
     mode = budget["mode"]
     if mode == "dynamic":
         kh, masses = budgets(q, k, S, G, gamma, block, scale, budget.get("last_blocks", 1))

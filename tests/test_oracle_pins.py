@@ -418,3 +418,46 @@ def test_pipeline_budget_modes():
     for h in range(H):
         np.testing.assert_allclose(many["masses"][h], O.last_blocks_masses(
             q[h], k[O.kv_head_of(h, H, Hkv)], B, 1 / math.sqrt(d), 3), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- sequence-level skip of the scoring
+def _brute_strided_scores(qp, kp, block, scale, s):
+    N = qp.shape[0]
+    nb = N // block
+    S = [[-math.inf] * nb for _ in range(nb)]
+    for i in range(N):
+        if i % s != s - 1:
+            continue
+        for j in range(i + 1):
+            v = _brute_logit(qp[i], kp[j], scale)
+            if v > S[i // block][j // block]:
+                S[i // block][j // block] = v
+    return np.array(S)
+
+
+@pytest.mark.parametrize("s", [2, 4])
+def test_strided_scores_bruteforce(s):
+    qp, kp = _rand((1, 32, 3), 60), _rand((1, 32, 3), 61)
+    got = O.proxy_scores(qp, kp, 8, 0.5, query_stride=s)[0]
+    np.testing.assert_allclose(got, _brute_strided_scores(qp[0], kp[0], 8, 0.5, s), rtol=1e-12)
+
+
+def test_strided_scores_bound_and_stride_one():
+    qp, kp = _rand((2, 64, 4), 62), _rand((2, 64, 4), 63)
+    full = O.proxy_scores(qp, kp, 16, 0.3)
+    np.testing.assert_array_equal(O.proxy_scores(qp, kp, 16, 0.3, query_stride=1), full)
+    for s in (2, 4, 8, 16):
+        sub = O.proxy_scores(qp, kp, 16, 0.3, query_stride=s)
+        assert np.all(sub <= full)                         # a max over fewer queries
+        assert np.all(np.isneginf(sub) == np.isneginf(full))   # same causal support
+        # stride = block: only the block's last query, which sees every key of the row
+        if s == 16:
+            for I in range(4):
+                i = (I + 1) * 16 - 1
+                row = 0.3 * qp[0, i] @ kp[0, : i + 1].T
+                np.testing.assert_allclose(sub[0, I, : I + 1], row.reshape(I + 1, 16).max(axis=1))
+
+
+def test_strided_scores_reject_bad_stride():
+    with pytest.raises(ValueError):
+        O.proxy_score_row(np.zeros((32, 2)), np.zeros((32, 2)), 0, 16, 1.0, query_stride=3)
