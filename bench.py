@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--score-stride", type=int, default=1,
+                    help="sequence-level skip of the proxy scoring: score every s-th query "
+                         "(1, 2 or 4; 1 = every query, the default)")
     ap.add_argument("--budget", default="dynamic:1",
                     help="budget variant: dynamic:M (probe the last M query blocks; the method's "
                          "own budget, M=1 by default), fixed:K or ratio:R")
@@ -90,7 +93,8 @@ def profiled_traffic(workload):
         return None
 
 
-def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_kind="dynamic"):
+def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_kind="dynamic",
+                 score_stride=1):
     """Time the CPU oracle on a bounded sample and scale it to the full step.
 
     Sample: a token slice of the pooling, three query-block rows of the proxy
@@ -128,7 +132,7 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_k
     kbar0 = O.round_bf16(kg.mean(axis=0))
     tiles = 0
     for I in rows:
-        O.proxy_score_row(qbar0, kbar0, I, B, scale)
+        O.proxy_score_row(qbar0, kbar0, I, B, scale, score_stride)
         tiles += I + 1
     est["score"] = (time.perf_counter() - t) * (G * nb * (nb + 1) / 2) / tiles
     del qg, kg
@@ -200,9 +204,11 @@ def main():
     dev = {n: torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("q", "k", "v")}
     torch.cuda.synchronize()
     kind, _, val = a.budget.partition(":")
-    budget = {"dynamic": lambda: pxa.Budget.dynamic(int(val or 1)),
-              "fixed": lambda: pxa.Budget.fixed(int(val)),
-              "ratio": lambda: pxa.Budget.ratio_of(float(val))}[kind]()
+    budget = {"dynamic": lambda: pxa.Options.dynamic(int(val or 1)),
+              "fixed": lambda: pxa.Options.fixed(int(val)),
+              "ratio": lambda: pxa.Options.ratio_of(float(val))}[kind]()
+    import dataclasses
+    budget = dataclasses.replace(budget, score_stride=a.score_stride)
     budget_desc = {"mode": kind, **({"last_blocks": budget.last_blocks} if kind == "dynamic" else
                                     {"blocks": budget.fixed_blocks} if kind == "fixed" else
                                     {"ratio": budget.ratio})}
@@ -230,7 +236,7 @@ def main():
         attn(dev["q"], dev["k"], dev["v"], out=o)
         for _ in range(a.steps):
             pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
-            pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
+            pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.scores)
             budget_stage()
             select_stage()
             pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
@@ -265,7 +271,7 @@ def main():
         evs[0].record(stream)
         pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
         evs[1].record(stream)
-        pxa.pxa_proxy_score(cfg, attn.qbar, attn.kbar, attn.scores)
+        pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.scores)
         evs[2].record(stream)
         budget_stage()
         evs[3].record(stream)
@@ -325,10 +331,43 @@ def main():
     density = (n_kept - 0.5 * n_diag) / causal_half_blocks
     f_kept = (n_kept - n_diag) * 4.0 * B * B * d + n_diag * 2.0 * B * B * d
     f_dense = 2.0 * N * N * d * H
-    f_score = G * (nb * (nb + 1) / 2) * 2.0 * B * B * d
+    f_score = G * (nb * (nb + 1) / 2) * 2.0 * B * B * d / a.score_stride
     tflops = lambda f, ms: f / (ms * 1e-3) / 1e12  # noqa: E731
     kept_tflops = tflops(f_kept, stage["sparse"])
     est_ms = stage["pool"] + stage["score"] + stage["budget"] + stage["select"]
+
+    # the skip is an approximation: compare its mask with the every-query mask
+    stride_cmp = None
+    if a.score_stride > 1:
+        full = dataclasses.replace(budget, score_stride=1)
+        S1 = torch.empty_like(attn.scores)
+        pxa.pxa_proxy_score_ex(cfg, full, attn.qbar, attn.kbar, S1)
+        kh1 = torch.empty_like(attn.k_h)
+        rp1 = torch.empty_like(attn.row_ptr)
+        ci1 = torch.empty_like(attn.col_idx)
+        if kind != "ratio":
+            pxa.pxa_budget_estimate_ex(cfg, full, dev["q"], dev["k"], S1, kh1,
+                                       torch.empty_like(attn.masses), attn.ws[L.budget_ws:],
+                                       ws_bytes=bws_bytes)
+        pxa.pxa_block_select_ex(cfg, full, S1, None if kind == "ratio" else kh1, rp1, ci1,
+                                attn.ws[L.select_ws:], ws_bytes=pxa.pxa_select_workspace_bytes(cfg))
+
+        def dense_mask(rp_t, ci_t):
+            rows = torch.repeat_interleave(torch.arange(H * nb, device="cuda"),
+                                           (rp_t[1:] - rp_t[:-1]).long())
+            m = torch.zeros(H * nb * nb, dtype=torch.bool, device="cuda")
+            m[rows * nb + ci_t[: int(rp_t[-1])].long()] = True
+            return m
+
+        m_s, m_1 = dense_mask(attn.row_ptr, attn.col_idx), dense_mask(rp1, ci1)
+        causal_total = H * nb * (nb + 1) // 2
+        diff = int((m_s ^ m_1).sum())
+        stride_cmp = {"causal_blocks_differing": diff,
+                      "fraction_identical": round(1.0 - diff / causal_total, 5),
+                      "kept_every_query": int(m_1.sum()), "kept_strided": int(m_s.sum()),
+                      "kept_in_both": int((m_s & m_1).sum())}
+        del S1, kh1, rp1, ci1, m_s, m_1
+        log(f"strided mask vs every-query mask: {stride_cmp}")
     pool_bytes = (H + Hkv + 2 * G) * N * d * 2
     budget_bytes = Hkv * N * d * 2 + H * B * d * 2 + H * nb * B * 4 * 2
     select_bytes = G * nb * nb * 4 + H * nb * 4 * 3 + n_kept * 4
@@ -345,7 +384,8 @@ def main():
                 samp.append((h, I, ci[rp[r]:rp[r + 1]].astype(np.int64)))
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(cfg, x, samp, n_kept, budget_s=a.cpu_budget_s,
-                           last_blocks=budget.last_blocks, budget_kind=kind)
+                           last_blocks=budget.last_blocks, budget_kind=kind,
+                           score_stride=a.score_stride)
         cpu["value"] = round(cpu["value"], 1)
 
     res = {
@@ -355,13 +395,15 @@ def main():
         "data": "synthetic (seeded generator, bf16, inputs resident in HBM)",
         "config": {"workload": f"{wl.name}: {wl.description}", "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": d, "seq_len": N, "block": B, "num_proxies": G, "gamma": gamma,
-                   "batch": 1, "budget": budget_desc, "input_sha256_16": digest},
+                   "batch": 1, "budget": budget_desc, "score_stride": a.score_stride,
+                   "input_sha256_16": digest},
         "speedup_vs_dense": round(dense_ms / ms_step, 3),
         "dense_ms": round(dense_ms, 3),
         "torch_sdpa_dense": sdpa,
         "estimation_ms": round(est_ms, 3),
         "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
         "kept_density": round(density, 4),
+        "mask_vs_every_query_scoring": stride_cmp,
         "k_h": kh.tolist() if kind != "ratio" else None,
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "kept_block_mfma_util": round(kept_tflops / PEAK_BF16_TFLOPS, 4),

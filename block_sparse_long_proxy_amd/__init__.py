@@ -10,8 +10,8 @@ include/pxa.h); this package only marshals torch tensors to it.
     o = attn(q, k, v)                  # q [H,N,d], k/v [Hkv,N,d] bf16 on the GPU
     attn.k_h, attn.row_ptr, attn.col_idx, attn.scores   # the mask it used
 
-Budget variants: ProxyAttn(cfg, Budget.dynamic(last_blocks=4)),
-Budget.fixed(blocks=64), Budget.ratio_of(0.1).
+Method variants: ProxyAttn(cfg, Options.dynamic(last_blocks=4)),
+Options.fixed(blocks=64), Options.ratio_of(0.1), Options.dynamic(score_stride=2).
 """
 from ._binding import (  # noqa: F401
     Config, PxaError, load_library, LIB_PATH,
@@ -19,8 +19,8 @@ from ._binding import (  # noqa: F401
     pxa_get_workspace_layout, pxa_budget_workspace_bytes, pxa_select_workspace_bytes,
     pxa_max_col_entries, pxa_prefill, pxa_proxy_pool, pxa_proxy_score, pxa_budget_estimate,
     pxa_block_select, pxa_sparse_prefill, pxa_dense_prefill,
-    Budget, PXA_BUDGET_DYNAMIC, PXA_BUDGET_FIXED, PXA_BUDGET_RATIO, PXA_MAX_PROBE_BLOCKS,
-    pxa_validate_budget, pxa_workspace_bytes_ex, pxa_get_workspace_layout_ex,
+    Options, PXA_BUDGET_DYNAMIC, PXA_BUDGET_FIXED, PXA_BUDGET_RATIO, PXA_MAX_PROBE_BLOCKS,
+    pxa_validate_options, pxa_proxy_score_ex, pxa_workspace_bytes_ex, pxa_get_workspace_layout_ex,
     pxa_budget_workspace_bytes_ex, pxa_prefill_ex, pxa_budget_estimate_ex, pxa_block_select_ex,
 )
 
@@ -28,12 +28,12 @@ from ._binding import (  # noqa: F401
 class ProxyAttn:
     """Whole-pipeline call with a persistent workspace and views of its parts."""
 
-    def __init__(self, cfg: Config, budget: "Budget | None" = None, device="cuda"):
+    def __init__(self, cfg: Config, opts: "Options | None" = None, device="cuda"):
         import torch
         self.cfg = cfg
-        self.budget = budget
+        self.opts = opts
         load_library()
-        L = pxa_get_workspace_layout_ex(cfg, budget)
+        L = pxa_get_workspace_layout_ex(cfg, opts)
         self.layout = L
         self.ws = torch.empty(L.total, dtype=torch.uint8, device=device)
         nb, H, G, N, d = cfg.nb, cfg.num_heads, cfg.num_proxies, cfg.seq_len, cfg.head_dim
@@ -54,7 +54,7 @@ class ProxyAttn:
     def __call__(self, q, k, v, out=None, stream=None):
         import torch
         o = out if out is not None else torch.empty_like(q)
-        pxa_prefill_ex(self.cfg, self.budget, q, k, v, o, self.ws, stream=stream)
+        pxa_prefill_ex(self.cfg, self.opts, q, k, v, o, self.ws, stream=stream)
         return o
 
     def dense(self, q, k, v, out=None, stream=None):

@@ -47,9 +47,10 @@ PXA_BUDGET_RATIO = 2
 PXA_MAX_PROBE_BLOCKS = 64
 
 
-class pxa_budget(ctypes.Structure):
-    _fields_ = [("mode", ctypes.c_int32), ("last_blocks", ctypes.c_int32),
-                ("fixed_blocks", ctypes.c_int32), ("ratio", ctypes.c_float)]
+class pxa_options(ctypes.Structure):
+    _fields_ = [("budget_mode", ctypes.c_int32), ("last_blocks", ctypes.c_int32),
+                ("fixed_blocks", ctypes.c_int32), ("ratio", ctypes.c_float),
+                ("score_stride", ctypes.c_int32)]
 
 
 class pxa_workspace_layout(ctypes.Structure):
@@ -60,7 +61,7 @@ class pxa_workspace_layout(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _CFG = ctypes.POINTER(pxa_config)
-_BUD = ctypes.POINTER(pxa_budget)
+_OPT = ctypes.POINTER(pxa_options)
 _SIGNATURES = {
     "pxa_abi_version": (ctypes.c_int, []),
     "pxa_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -78,13 +79,14 @@ _SIGNATURES = {
     "pxa_block_select": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_sparse_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pxa_dense_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
-    "pxa_validate_budget": (ctypes.c_int, [_CFG, _BUD]),
-    "pxa_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _BUD]),
-    "pxa_get_workspace_layout_ex": (ctypes.c_int, [_CFG, _BUD, ctypes.POINTER(pxa_workspace_layout)]),
-    "pxa_budget_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _BUD]),
-    "pxa_prefill_ex": (ctypes.c_int, [_CFG, _BUD, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "pxa_budget_estimate_ex": (ctypes.c_int, [_CFG, _BUD, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "pxa_block_select_ex": (ctypes.c_int, [_CFG, _BUD, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_validate_options": (ctypes.c_int, [_CFG, _OPT]),
+    "pxa_proxy_score_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P]),
+    "pxa_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
+    "pxa_get_workspace_layout_ex": (ctypes.c_int, [_CFG, _OPT, ctypes.POINTER(pxa_workspace_layout)]),
+    "pxa_budget_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
+    "pxa_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_budget_estimate_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_block_select_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -133,32 +135,34 @@ class Config:
 
 
 @dataclass(frozen=True)
-class Budget:
-    """A budget variant (include/pxa.h, pxa_budget).  Budget() is the default:
-    the dynamic budget probed on the last query block."""
-    mode: int = PXA_BUDGET_DYNAMIC
+class Options:
+    """Method variants (include/pxa.h, pxa_options).  Options() is the default:
+    the dynamic budget probed on the last query block, every query scored."""
+    budget_mode: int = PXA_BUDGET_DYNAMIC
     last_blocks: int = 1
     fixed_blocks: int = 0
     ratio: float = 0.0
+    score_stride: int = 1
 
     @staticmethod
-    def dynamic(last_blocks: int = 1) -> "Budget":
-        return Budget(PXA_BUDGET_DYNAMIC, last_blocks=last_blocks)
+    def dynamic(last_blocks: int = 1, score_stride: int = 1) -> "Options":
+        return Options(PXA_BUDGET_DYNAMIC, last_blocks=last_blocks, score_stride=score_stride)
 
     @staticmethod
-    def fixed(blocks: int) -> "Budget":
-        return Budget(PXA_BUDGET_FIXED, fixed_blocks=blocks)
+    def fixed(blocks: int, score_stride: int = 1) -> "Options":
+        return Options(PXA_BUDGET_FIXED, fixed_blocks=blocks, score_stride=score_stride)
 
     @staticmethod
-    def ratio_of(r: float) -> "Budget":
-        return Budget(PXA_BUDGET_RATIO, ratio=r)
+    def ratio_of(r: float, score_stride: int = 1) -> "Options":
+        return Options(PXA_BUDGET_RATIO, ratio=r, score_stride=score_stride)
 
-    def c(self) -> pxa_budget:
-        return pxa_budget(self.mode, self.last_blocks, self.fixed_blocks, self.ratio)
+    def c(self) -> pxa_options:
+        return pxa_options(self.budget_mode, self.last_blocks, self.fixed_blocks, self.ratio,
+                           self.score_stride)
 
 
-def _bref(budget: Optional[Budget]):
-    return None if budget is None else ctypes.byref(budget.c())
+def _bref(opts: Optional[Options]):
+    return None if opts is None else ctypes.byref(opts.c())
 
 
 def _check(rc: int, where: str) -> None:
@@ -302,48 +306,55 @@ def pxa_dense_prefill(cfg: Config, q, k, v, o, stream=None) -> None:
         _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill")
 
 
-# ---------------------------------------------------------------- budget variants
-def pxa_validate_budget(cfg: Config, budget: Optional[Budget]) -> int:
-    return load_library().pxa_validate_budget(ctypes.byref(cfg.c()), _bref(budget))
+# ---------------------------------------------------------------- method variants
+def pxa_proxy_score_ex(cfg: Config, opts: Optional[Options], qbar, kbar, scores,
+                       stream=None) -> None:
+    _check(load_library().pxa_proxy_score_ex(
+        ctypes.byref(cfg.c()), _bref(opts), _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"),
+        _tp(scores, "f32", "scores"), _stream(stream)), "pxa_proxy_score_ex")
 
 
-def pxa_workspace_bytes_ex(cfg: Config, budget: Optional[Budget]) -> int:
-    return load_library().pxa_workspace_bytes_ex(ctypes.byref(cfg.c()), _bref(budget))
+def pxa_validate_options(cfg: Config, opts: Optional[Options]) -> int:
+    return load_library().pxa_validate_options(ctypes.byref(cfg.c()), _bref(opts))
 
 
-def pxa_get_workspace_layout_ex(cfg: Config, budget: Optional[Budget]) -> pxa_workspace_layout:
+def pxa_workspace_bytes_ex(cfg: Config, opts: Optional[Options]) -> int:
+    return load_library().pxa_workspace_bytes_ex(ctypes.byref(cfg.c()), _bref(opts))
+
+
+def pxa_get_workspace_layout_ex(cfg: Config, opts: Optional[Options]) -> pxa_workspace_layout:
     out = pxa_workspace_layout()
-    _check(load_library().pxa_get_workspace_layout_ex(ctypes.byref(cfg.c()), _bref(budget),
+    _check(load_library().pxa_get_workspace_layout_ex(ctypes.byref(cfg.c()), _bref(opts),
                                                       ctypes.byref(out)),
            "pxa_get_workspace_layout_ex")
     return out
 
 
-def pxa_budget_workspace_bytes_ex(cfg: Config, budget: Optional[Budget]) -> int:
-    return load_library().pxa_budget_workspace_bytes_ex(ctypes.byref(cfg.c()), _bref(budget))
+def pxa_budget_workspace_bytes_ex(cfg: Config, opts: Optional[Options]) -> int:
+    return load_library().pxa_budget_workspace_bytes_ex(ctypes.byref(cfg.c()), _bref(opts))
 
 
-def pxa_prefill_ex(cfg: Config, budget: Optional[Budget], q, k, v, o, ws, ws_bytes=None,
+def pxa_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, ws, ws_bytes=None,
                    stream=None) -> None:
     _check(load_library().pxa_prefill_ex(
-        ctypes.byref(cfg.c()), _bref(budget), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
+        ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
         _stream(stream)), "pxa_prefill_ex")
 
 
-def pxa_budget_estimate_ex(cfg: Config, budget: Optional[Budget], q, k, scores, k_h, masses, ws,
+def pxa_budget_estimate_ex(cfg: Config, opts: Optional[Options], q, k, scores, k_h, masses, ws,
                            ws_bytes=None, stream=None) -> None:
     _check(load_library().pxa_budget_estimate_ex(
-        ctypes.byref(cfg.c()), _bref(budget), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
+        ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"), _tp(masses, "f32", "masses"),
         _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes) if ws is not None else 0, _stream(stream)),
         "pxa_budget_estimate_ex")
 
 
-def pxa_block_select_ex(cfg: Config, budget: Optional[Budget], scores, k_h, row_ptr, col_idx, ws,
+def pxa_block_select_ex(cfg: Config, opts: Optional[Options], scores, k_h, row_ptr, col_idx, ws,
                         ws_bytes=None, stream=None, row_order=None) -> None:
     _check(load_library().pxa_block_select_ex(
-        ctypes.byref(cfg.c()), _bref(budget), _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"),
+        ctypes.byref(cfg.c()), _bref(opts), _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"),
         _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
         _tp(row_order, "i32", "row_order"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
         _stream(stream)), "pxa_block_select_ex")

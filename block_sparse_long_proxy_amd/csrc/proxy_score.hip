@@ -6,6 +6,11 @@
 // Causal prefill: in the diagonal block only keys j <= i count; blocks above
 // the diagonal get -inf.
 //
+// With a query stride s (the sequence-level skip of section 5, read as
+// scoring every s-th query of a block: offsets s-1, 2s-1, ..., 127) a
+// workgroup serves s consecutive rows, 128/s queries each, so the per-tile
+// work and the reuse of each K tile stay those of s = 1.
+//
 // One workgroup of four waves per proxy g and query-block row I, two
 // workgroups per CU (they run out of phase, so one's maxima and barriers
 // overlap the other's MFMAs).  Key tiles J = 0..I stream through a two-deep
@@ -24,50 +29,78 @@ namespace pxa {
 
 constexpr int kScoreBufs = 2;                  // K tile in use + the next one in flight
 
-template <int D>
+// STRIDE s: the block's queries at offsets s-1, 2s-1, ..., 127 are scored
+// (128/s of them, in QC = 4/s chunks of 32); s = 1 scores every query.
+template <int D, int STRIDE>
 __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
     int G, int N, float scale) {
+  // STRIDE s: rows I0, I0-1, ..., I0-s+1 share the workgroup, each with its
+  // 128/s scored queries (offsets s-1, 2s-1, ..., 127), so every wave still
+  // holds 4 chunks of 32 queries and each K tile feeds the same MFMA work.
+  constexpr int R = STRIDE;          // rows per workgroup
+  constexpr int QC = 4 / STRIDE;     // 32-query chunks per row
+  static_assert(QC * STRIDE == 4, "stride 1, 2 or 4");
   __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
-  __shared__ float wm[2][kWaves][64];            // per-wave maxima of one 64-tile chunk
+  __shared__ float wm[2][R][kWaves][64];         // per-wave maxima of one 64-tile chunk
 
   const int nb = N / kBlock;
   const int g = (int)(blockIdx.x % G);
-  const int I = nb - 1 - (int)(blockIdx.x / G);  // longest rows first
+  const int I0 = nb - 1 - R * (int)(blockIdx.x / G);   // top row; longest rows first
   const int ws = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // keys 32 ws ..
   const int l = threadIdx.x & 63;
   const int hi = l >> 5;
   constexpr size_t kTile = (size_t)kBlock * D;
 
+  // chunk c serves row I0 - c / QC; the lane's query offset inside that block
+  auto qoff = [&](int c) { return STRIDE * (32 * (c % QC) + (l & 31)) + STRIDE - 1; };
   bf16x8 qf[4][D / 16];
 #pragma unroll
-  for (int qs = 0; qs < 4; ++qs)
-    load_qfrag<D>(qbar + ((size_t)g * N + (size_t)I * kBlock + 32 * qs + (l & 31)) * D, qf[qs]);
+  for (int c = 0; c < 4; ++c) {
+    const int Ir = I0 - c / QC;
+    if (Ir >= 0) {
+      load_qfrag<D>(qbar + ((size_t)g * N + (size_t)Ir * kBlock + qoff(c)) * D, qf[c]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) qf[c][s] = bf16x8{};
+    }
+  }
   const __bf16* kb = uniform_ptr(kbar + (size_t)g * N * D);
-  float* srow = scores + ((size_t)g * nb + I) * nb;
-  for (int J = I + 1 + threadIdx.x; J < nb; J += kThreads) srow[J] = -INFINITY;
-  // Wave 0: combine chunk c (tiles 64c .. 64c+63) of the four slices.
-  auto store_chunk = [&](int c) {
-    if (threadIdx.x < 64) {
-      const int J = 64 * c + l;
-      if (J <= I) {
-        const float* p = &wm[c & 1][0][l];
-        srow[J] = fmaxf(fmaxf(p[0], p[64]), fmaxf(p[128], p[192])) * scale;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int Ir = I0 - r;
+    if (Ir < 0) continue;
+    float* srow = scores + ((size_t)g * nb + Ir) * nb;
+    for (int J = Ir + 1 + threadIdx.x; J < nb; J += kThreads) srow[J] = -INFINITY;
+  }
+  // Threads 0..64R-1: combine chunk cc (tiles 64cc .. 64cc+63) of the four
+  // key slices, for row I0 - (thread / 64).
+  auto store_chunk = [&](int cc) {
+    if (threadIdx.x < 64 * R) {
+      const int r = threadIdx.x >> 6;
+      const int Ir = I0 - r;
+      const int J = 64 * cc + l;
+      if (Ir >= 0 && J <= Ir) {
+        const float* p = &wm[cc & 1][r][0][l];
+        scores[((size_t)g * nb + Ir) * nb + J] =
+            fmaxf(fmaxf(p[0], p[64]), fmaxf(p[128], p[192])) * scale;
       }
     }
   };
 
   tile_load_lds<D, false>(kb, kt[0]);
-  float keep = -INFINITY;                        // this wave's max of tile J, in lane J mod 64
-  for (int J = 0; J <= I; ++J) {
+  float keep[R];                                 // this wave's max of tile J per row, lane J mod 64
+#pragma unroll
+  for (int r = 0; r < R; ++r) keep[r] = -INFINITY;
+  for (int J = 0; J <= I0; ++J) {
     wait_vmem();       // this thread's part of tile J (the only copy in flight)
     __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
-    if (J + 1 <= I) tile_load_lds<D, false>(kb + (size_t)(J + 1) * kTile, kt[(J + 1) % kScoreBufs]);
+    if (J + 1 <= I0) tile_load_lds<D, false>(kb + (size_t)(J + 1) * kTile, kt[(J + 1) % kScoreBufs]);
     if (J > 0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
     const __bf16* cur = kt[J % kScoreBufs];
     f32x16 acc[4];
 #pragma unroll
-    for (int qs = 0; qs < 4; ++qs) acc[qs] = zero16();
+    for (int c = 0; c < 4; ++c) acc[c] = zero16();
     // The fragment of k-step s+1 is read before the four products of step s
     // issue (scheduling barriers keep that order; the default schedule reuses
     // one register set and waits for every read).
@@ -78,46 +111,60 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       if (s + 1 < D / 16) an = ktile_frag<D>(cur, ws, s + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs) acc[qs] = mfma32(a, qf[qs][s], acc[qs]);
+      for (int c = 0; c < 4; ++c) acc[c] = mfma32(a, qf[c][s], acc[c]);
       __builtin_amdgcn_sched_barrier(0);
       a = an;
     }
-    float mx = -INFINITY;
-    if (J == I) {   // causal: key 32 ws + row(r) must not exceed query 32 qs + l%32
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs)
+    for (int r = 0; r < R; ++r) {
+      const int Ir = I0 - r;
+      float mx = -INFINITY;
+      if (J < Ir) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * ws + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key <= 32 * qs + (l & 31)) mx = fmaxf(mx, acc[qs][r]);
-        }
-    } else {
+        for (int cc = 0; cc < QC; ++cc)
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs)
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[r * QC + cc][e]);
+      } else if (J == Ir) {   // causal: key 32 ws + row(e) must not exceed the lane's query
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[qs][r]);
+        for (int cc = 0; cc < QC; ++cc)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = 32 * ws + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (key <= qoff(r * QC + cc)) mx = fmaxf(mx, acc[r * QC + cc][e]);
+          }
+      }                       // J > Ir: above that row's diagonal, nothing counts
+      mx = wave_max_uniform(mx);
+      if (l == (J & 63)) keep[r] = mx;
     }
-    mx = wave_max_uniform(mx);
-    if (l == (J & 63)) keep = mx;
-    if ((J & 63) == 63 || J == I) {
-      wm[(J >> 6) & 1][ws][l] = keep;
-      keep = -INFINITY;
+    if ((J & 63) == 63 || J == I0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        wm[(J >> 6) & 1][r][ws][l] = keep[r];
+        keep[r] = -INFINITY;
+      }
     }
   }
   __syncthreads();
-  store_chunk(I >> 6);
+  store_chunk(I0 >> 6);
 }
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,
                               float* scores, hipStream_t stream) {
   const int nb = a.N / kBlock;
-  const dim3 grid(a.G * nb), block(kThreads);
-  if (a.D == 64)
-    hipLaunchKernelGGL(proxy_score_kernel<64>, grid, block, 0, stream, (const __bf16*)qbar,
-                       (const __bf16*)kbar, scores, a.G, a.N, a.scale);
-  else
-    hipLaunchKernelGGL(proxy_score_kernel<128>, grid, block, 0, stream, (const __bf16*)qbar,
-                       (const __bf16*)kbar, scores, a.G, a.N, a.scale);
+  const dim3 grid(a.G * ((nb + a.score_stride - 1) / a.score_stride)), block(kThreads);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)qbar, (const __bf16*)kbar,
+                       scores, a.G, a.N, a.scale);
+  };
+  if (a.D == 64) {
+    if (a.score_stride == 4) go(proxy_score_kernel<64, 4>);
+    else if (a.score_stride == 2) go(proxy_score_kernel<64, 2>);
+    else go(proxy_score_kernel<64, 1>);
+  } else {
+    if (a.score_stride == 4) go(proxy_score_kernel<128, 4>);
+    else if (a.score_stride == 2) go(proxy_score_kernel<128, 2>);
+    else go(proxy_score_kernel<128, 1>);
+  }
   return hipGetLastError();
 }
 

@@ -39,11 +39,12 @@ int check_config(const pxa_config* c) {
   return PXA_OK;
 }
 
-// Budget variant check against a valid configuration; NULL is the default.
-int check_budget(const pxa_config* c, const pxa_budget* b) {
+// Method-variant check against a valid configuration; NULL is the default.
+int check_budget(const pxa_config* c, const pxa_options* b) {
   if (!b) return PXA_OK;
   const int nb = c->seq_len / pxa::kBlockTokens;
-  switch (b->mode) {
+  if (b->score_stride != 1 && b->score_stride != 2 && b->score_stride != 4) return PXA_EINVAL;
+  switch (b->budget_mode) {
     case PXA_BUDGET_DYNAMIC:
       if (b->last_blocks < 1 || b->last_blocks > nb || b->last_blocks > PXA_MAX_PROBE_BLOCKS)
         return PXA_EINVAL;
@@ -57,12 +58,12 @@ int check_budget(const pxa_config* c, const pxa_budget* b) {
   }
 }
 
-int check_all(const pxa_config* c, const pxa_budget* b) {
+int check_all(const pxa_config* c, const pxa_options* b) {
   const int rc = check_config(c);
   return rc != PXA_OK ? rc : check_budget(c, b);
 }
 
-pxa::LaunchArgs args_of(const pxa_config* c, const pxa_budget* b = nullptr) {
+pxa::LaunchArgs args_of(const pxa_config* c, const pxa_options* b = nullptr) {
   pxa::LaunchArgs a;
   a.H = c->num_heads;
   a.Hkv = c->num_kv_heads;
@@ -72,10 +73,11 @@ pxa::LaunchArgs args_of(const pxa_config* c, const pxa_budget* b = nullptr) {
   a.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / std::sqrt((float)c->head_dim);
   a.gamma = c->gamma;
   if (b) {
-    a.budget_mode = b->mode;
-    a.last_blocks = b->mode == PXA_BUDGET_DYNAMIC ? b->last_blocks : 1;
+    a.budget_mode = b->budget_mode;
+    a.last_blocks = b->budget_mode == PXA_BUDGET_DYNAMIC ? b->last_blocks : 1;
     a.fixed_blocks = b->fixed_blocks;
     a.ratio = b->ratio;
+    a.score_stride = b->score_stride;
   }
   return a;
 }
@@ -106,7 +108,7 @@ int hip_rc(hipError_t e) {
   return PXA_EHIP;
 }
 
-void layout_of(const pxa_config* c, const pxa_budget* b, pxa_workspace_layout* L) {
+void layout_of(const pxa_config* c, const pxa_options* b, pxa_workspace_layout* L) {
   const pxa::LaunchArgs a = args_of(c, b);
   const size_t nb = (size_t)a.N / pxa::kBlockTokens;
   size_t off = 0;
@@ -182,18 +184,18 @@ size_t pxa_max_col_entries(const pxa_config* cfg) {
   return (size_t)cfg->num_heads * nb * (nb + 1) / 2;
 }
 
-int pxa_validate_budget(const pxa_config* cfg, const pxa_budget* budget) {
+int pxa_validate_options(const pxa_config* cfg, const pxa_options* budget) {
   return check_all(cfg, budget);
 }
 
-size_t pxa_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget) {
+size_t pxa_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* budget) {
   if (check_all(cfg, budget) != PXA_OK) return 0;
   pxa_workspace_layout L;
   layout_of(cfg, budget, &L);
   return L.total;
 }
 
-int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_budget* budget,
+int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_options* budget,
                                 pxa_workspace_layout* out) {
   const int rc = check_all(cfg, budget);
   if (rc != PXA_OK) return rc;
@@ -202,7 +204,7 @@ int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_budget* budget,
   return PXA_OK;
 }
 
-size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget) {
+size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* budget) {
   if (check_all(cfg, budget) != PXA_OK) return 0;
   return pxa::budget_ws_bytes(args_of(cfg, budget));
 }
@@ -215,15 +217,21 @@ int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k, void* qb
   return hip_rc(pxa::launch_proxy_pool(args_of(cfg), q, k, qbar, kbar, (hipStream_t)stream));
 }
 
-int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar, float* scores,
-                    void* stream) {
-  int rc = check_config(cfg);
+int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const void* qbar,
+                       const void* kbar, float* scores, void* stream) {
+  int rc = check_all(cfg, opts);
   if (rc) return rc;
   if ((rc = ptrs_ok({{qbar, 16}, {kbar, 16}, {scores, 4}}))) return rc;
-  return hip_rc(pxa::launch_proxy_score(args_of(cfg), qbar, kbar, scores, (hipStream_t)stream));
+  return hip_rc(pxa::launch_proxy_score(args_of(cfg, opts), qbar, kbar, scores,
+                                        (hipStream_t)stream));
 }
 
-int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar, float* scores,
+                    void* stream) {
+  return pxa_proxy_score_ex(cfg, nullptr, qbar, kbar, scores, stream);
+}
+
+int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_options* budget, const void* q,
                            const void* k, const float* scores, int32_t* k_h, float* masses,
                            void* ws, size_t ws_bytes, void* stream) {
   int rc = check_all(cfg, budget);
@@ -244,7 +252,7 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k, con
   return pxa_budget_estimate_ex(cfg, nullptr, q, k, scores, k_h, masses, ws, ws_bytes, stream);
 }
 
-int pxa_block_select_ex(const pxa_config* cfg, const pxa_budget* budget, const float* scores,
+int pxa_block_select_ex(const pxa_config* cfg, const pxa_options* budget, const float* scores,
                         const int32_t* k_h, int32_t* row_ptr, int32_t* col_idx,
                         int32_t* row_order, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_all(cfg, budget);
@@ -286,7 +294,7 @@ int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const
                                        true, (hipStream_t)stream));
 }
 
-int pxa_prefill_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* budget, const void* q,
                    const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                    void* stream) {
   int rc = check_all(cfg, budget);

@@ -19,6 +19,7 @@ struct LaunchArgs {
   int last_blocks = 1;    // dynamic budget: query blocks probed
   int fixed_blocks = 0;   // fixed budget: blocks per row
   float ratio = 0.f;      // ratio budget
+  int score_stride = 1;   // queries scored per block: 128 / score_stride
 };
 
 hipError_t launch_proxy_pool(const LaunchArgs& a, const void* q, const void* k, void* qbar,

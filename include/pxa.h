@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 2
+#define PXA_ABI_VERSION 3
 
 enum {
   PXA_OK = 0,
@@ -70,16 +70,20 @@ typedef struct pxa_config {
   float softmax_scale;   /* > 0, or <= 0 for 1/sqrt(d)                           */
 } pxa_config;
 
-/* Budget variants.  The method's own budget is DYNAMIC (section 4, step 2:
- * the last small portion of the query blocks probes each head's sparsity);
- * FIXED is the one-budget-for-all-heads comparison that step draws; RATIO is
- * the Top-K-by-proportion choice of the XAttention report (leeon-k.github.io,
- * section 2.2).  Every entry point that takes a `const pxa_budget*` reads NULL
- * as {PXA_BUDGET_DYNAMIC, 1, 0, 0}, the behaviour of the calls without _ex. */
+/* Method variants.  Budget: the method's own budget is DYNAMIC (section 4,
+ * step 2: the last small portion of the query blocks probes each head's
+ * sparsity); FIXED is the one-budget-for-all-heads comparison that step
+ * draws; RATIO is the Top-K-by-proportion choice of the XAttention report
+ * (leeon-k.github.io, section 2.2).  Scoring: score_stride s > 1 is the
+ * sequence-level skip that section 5 credits for the low estimation cost,
+ * read as scoring only every s-th query of a block (offsets s-1, 2s-1, ...,
+ * B-1) against every key -- an approximation of the s = 1 scores.  Every
+ * entry point that takes a `const pxa_options*` reads NULL as
+ * {PXA_BUDGET_DYNAMIC, 1, 0, 0, 1}, the behaviour of the calls without _ex. */
 enum { PXA_BUDGET_DYNAMIC = 0, PXA_BUDGET_FIXED = 1, PXA_BUDGET_RATIO = 2 };
 #define PXA_MAX_PROBE_BLOCKS 64
-typedef struct pxa_budget {
-  int32_t mode;          /* PXA_BUDGET_*                                         */
+typedef struct pxa_options {
+  int32_t budget_mode;   /* PXA_BUDGET_*                                         */
   int32_t last_blocks;   /* DYNAMIC: m, 1 <= m <= min(nb, PXA_MAX_PROBE_BLOCKS):
                             the masses average the last m*B queries              */
   int32_t fixed_blocks;  /* FIXED: k >= 1, every head keeps min(k, I+1) ranked
@@ -87,7 +91,8 @@ typedef struct pxa_budget {
   float ratio;           /* RATIO: 0 < r <= 1, row I keeps ceil(r*(I+1)) ranked
                             blocks (product rounded to fp32 first; at least 1)
                             plus the diagonal, the same for every head           */
-} pxa_budget;
+  int32_t score_stride;  /* 1, 2 or 4: queries scored per block = B / stride     */
+} pxa_options;
 
 /* Sizes and offsets of the whole-pipeline workspace (bytes from its start).
  * Intermediates are left there by pxa_prefill so a caller can inspect them. */
@@ -120,15 +125,15 @@ size_t pxa_budget_workspace_bytes(const pxa_config* cfg);
 size_t pxa_select_workspace_bytes(const pxa_config* cfg);
 /* Capacity col_idx must have: H * nb * (nb + 1) / 2 entries (every causal block). */
 size_t pxa_max_col_entries(const pxa_config* cfg);
-/* PXA_OK if cfg and budget (NULL: the default) are valid together, else the
+/* PXA_OK if cfg and opts (NULL: the defaults) are valid together, else the
  * code a call would return (PXA_EINVAL for a bad mode or parameter). */
-int pxa_validate_budget(const pxa_config* cfg, const pxa_budget* budget);
-/* The _ex queries size the workspaces for a budget variant (a probe of m
- * blocks needs m times the budget scratch); 0 if cfg or budget is invalid. */
-size_t pxa_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget);
-int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_budget* budget,
+int pxa_validate_options(const pxa_config* cfg, const pxa_options* opts);
+/* The _ex queries size the workspaces for a variant (a probe of m blocks
+ * needs m times the budget scratch); 0 if cfg or opts is invalid. */
+size_t pxa_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* opts);
+int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_options* opts,
                                 pxa_workspace_layout* out);
-size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* budget);
+size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* opts);
 
 /* ---- the pipeline ------------------------------------------------------- */
 
@@ -138,10 +143,10 @@ size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_budget* bu
  * pxa_get_workspace_layout reports. */
 int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
                 void* o, void* ws, size_t ws_bytes, void* stream);
-/* The same with a budget variant (NULL: as pxa_prefill); ws of at least
- * pxa_workspace_bytes_ex(cfg, budget) bytes.  FIXED writes k_h and leaves the
+/* The same with method variants (NULL: as pxa_prefill); ws of at least
+ * pxa_workspace_bytes_ex(cfg, opts) bytes.  FIXED writes k_h and leaves the
  * masses unwritten; RATIO writes neither (budget stage skipped). */
-int pxa_prefill_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
                    const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                    void* stream);
 
@@ -159,6 +164,11 @@ int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k,
  * for J > I.  bf16 MFMA products, fp32 accumulation. */
 int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar,
                     float* scores, void* stream);
+/* The same with the sequence-level skip: opts->score_stride = s scores only
+ * the queries at offsets s-1, 2s-1, ..., B-1 of each query block (every key
+ * of the causal range); s = 1 (or NULL opts) is pxa_proxy_score. */
+int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const void* qbar,
+                       const void* kbar, float* scores, void* stream);
 
 /* Step 2, dynamic budget (section 4, step 2: the last query block estimates
  * each head's block-level sparsity; the abstract's "block-aware dynamic budget
@@ -175,7 +185,7 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k,
  * ws: pxa_budget_workspace_bytes_ex.  FIXED: k_h[h] = fixed_blocks for every
  * head; only k_h is used (q, k, scores, masses, ws may be NULL).  RATIO has no
  * per-head budget: PXA_EINVAL. */
-int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_budget* budget, const void* q,
+int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
                            const void* k, const float* scores, int32_t* k_h, float* masses,
                            void* ws, size_t ws_bytes, void* stream);
 
@@ -201,7 +211,7 @@ int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* 
  * ceil(fl32(ratio * (I+1))) (at least 1, at most I+1) blocks of row I's
  * ranking plus the diagonal, and ignores k_h (which may be NULL); DYNAMIC and
  * FIXED use k_h as pxa_block_select does. */
-int pxa_block_select_ex(const pxa_config* cfg, const pxa_budget* budget, const float* scores,
+int pxa_block_select_ex(const pxa_config* cfg, const pxa_options* opts, const float* scores,
                         const int32_t* k_h, int32_t* row_ptr, int32_t* col_idx,
                         int32_t* row_order, void* ws, size_t ws_bytes, void* stream);
 

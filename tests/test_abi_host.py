@@ -33,13 +33,13 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 2
+    assert pxa.pxa_abi_version() == 3
 
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.pxa_config) == 32
     assert ctypes.sizeof(B.pxa_workspace_layout) == 11 * ctypes.sizeof(ctypes.c_size_t)
-    assert ctypes.sizeof(B.pxa_budget) == 16
+    assert ctypes.sizeof(B.pxa_options) == 20
     with open(os.path.join(ROOT, "include", "pxa.h")) as f:
         hdr = f.read()
     for name, val in (("PXA_BUDGET_DYNAMIC", 0), ("PXA_BUDGET_FIXED", 1), ("PXA_BUDGET_RATIO", 2)):
@@ -50,70 +50,84 @@ def test_struct_layouts_match_header():
 
 @pytest.mark.parametrize("budget,code", [
     (None, B.PXA_OK),
-    (pxa.Budget(), B.PXA_OK),
-    (pxa.Budget.dynamic(8), B.PXA_OK),               # m = nb
-    (pxa.Budget.dynamic(9), B.PXA_EINVAL),           # m > nb
-    (pxa.Budget.dynamic(0), B.PXA_EINVAL),
-    (pxa.Budget.fixed(1), B.PXA_OK),
-    (pxa.Budget.fixed(1000), B.PXA_OK),              # clamped per row by I+1
-    (pxa.Budget.fixed(0), B.PXA_EINVAL),
-    (pxa.Budget.ratio_of(1.0), B.PXA_OK),
-    (pxa.Budget.ratio_of(1e-9), B.PXA_OK),
-    (pxa.Budget.ratio_of(0.0), B.PXA_EINVAL),
-    (pxa.Budget.ratio_of(1.0001), B.PXA_EINVAL),
-    (pxa.Budget.ratio_of(float("nan")), B.PXA_EINVAL),
-    (pxa.Budget.ratio_of(float("inf")), B.PXA_EINVAL),
-    (pxa.Budget(mode=3), B.PXA_EINVAL),
-    (pxa.Budget(mode=-1), B.PXA_EINVAL),
+    (pxa.Options(), B.PXA_OK),
+    (pxa.Options.dynamic(8), B.PXA_OK),               # m = nb
+    (pxa.Options.dynamic(9), B.PXA_EINVAL),           # m > nb
+    (pxa.Options.dynamic(0), B.PXA_EINVAL),
+    (pxa.Options.fixed(1), B.PXA_OK),
+    (pxa.Options.fixed(1000), B.PXA_OK),              # clamped per row by I+1
+    (pxa.Options.fixed(0), B.PXA_EINVAL),
+    (pxa.Options.ratio_of(1.0), B.PXA_OK),
+    (pxa.Options.ratio_of(1e-9), B.PXA_OK),
+    (pxa.Options.ratio_of(0.0), B.PXA_EINVAL),
+    (pxa.Options.ratio_of(1.0001), B.PXA_EINVAL),
+    (pxa.Options.ratio_of(float("nan")), B.PXA_EINVAL),
+    (pxa.Options.ratio_of(float("inf")), B.PXA_EINVAL),
+    (pxa.Options(budget_mode=3), B.PXA_EINVAL),
+    (pxa.Options(budget_mode=-1), B.PXA_EINVAL),
+    (pxa.Options.dynamic(score_stride=2), B.PXA_OK),
+    (pxa.Options.ratio_of(0.2, score_stride=4), B.PXA_OK),
+    (pxa.Options.dynamic(score_stride=3), B.PXA_EINVAL),
+    (pxa.Options.dynamic(score_stride=8), B.PXA_EINVAL),
+    (pxa.Options.fixed(2, score_stride=0), B.PXA_EINVAL),
 ])
 def test_validate_budget_codes(budget, code):
-    assert pxa.pxa_validate_budget(_good(), budget) == code
+    assert pxa.pxa_validate_options(_good(), budget) == code
 
 
 def test_probe_cap_and_invalid_config_first():
     long = _good(seq_len=128 * 100)
-    assert pxa.pxa_validate_budget(long, pxa.Budget.dynamic(B.PXA_MAX_PROBE_BLOCKS)) == B.PXA_OK
-    assert pxa.pxa_validate_budget(long, pxa.Budget.dynamic(B.PXA_MAX_PROBE_BLOCKS + 1)) == B.PXA_EINVAL
-    assert pxa.pxa_validate_budget(_good(head_dim=96), pxa.Budget.ratio_of(2.0)) == B.PXA_EUNSUPPORTED
+    assert pxa.pxa_validate_options(long, pxa.Options.dynamic(B.PXA_MAX_PROBE_BLOCKS)) == B.PXA_OK
+    assert pxa.pxa_validate_options(long, pxa.Options.dynamic(B.PXA_MAX_PROBE_BLOCKS + 1)) == B.PXA_EINVAL
+    assert pxa.pxa_validate_options(_good(head_dim=96), pxa.Options.ratio_of(2.0)) == B.PXA_EUNSUPPORTED
 
 
 def test_budget_workspace_sizes():
     cfg = _good()
     base = pxa.pxa_budget_workspace_bytes(cfg)
     assert pxa.pxa_budget_workspace_bytes_ex(cfg, None) == base
-    assert pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Budget.dynamic(1)) == base
-    assert pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Budget.dynamic(4)) >= 4 * 8 * 8 * 128 * 4
+    assert pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Options.dynamic(1)) == base
+    assert pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Options.dynamic(4)) >= 4 * 8 * 8 * 128 * 4
     assert pxa.pxa_workspace_bytes_ex(cfg, None) == pxa.pxa_workspace_bytes(cfg)
-    assert pxa.pxa_workspace_bytes_ex(cfg, pxa.Budget.dynamic(4)) > pxa.pxa_workspace_bytes(cfg)
-    assert pxa.pxa_workspace_bytes_ex(cfg, pxa.Budget.dynamic(9)) == 0
-    L = pxa.pxa_get_workspace_layout_ex(cfg, pxa.Budget.dynamic(4))
-    assert L.select_ws >= L.budget_ws + pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Budget.dynamic(4))
-    assert L.total == pxa.pxa_workspace_bytes_ex(cfg, pxa.Budget.dynamic(4))
+    assert pxa.pxa_workspace_bytes_ex(cfg, pxa.Options.dynamic(4)) > pxa.pxa_workspace_bytes(cfg)
+    assert pxa.pxa_workspace_bytes_ex(cfg, pxa.Options.dynamic(9)) == 0
+    L = pxa.pxa_get_workspace_layout_ex(cfg, pxa.Options.dynamic(4))
+    assert L.select_ws >= L.budget_ws + pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Options.dynamic(4))
+    assert L.total == pxa.pxa_workspace_bytes_ex(cfg, pxa.Options.dynamic(4))
     with pytest.raises(pxa.PxaError) as e:
-        pxa.pxa_get_workspace_layout_ex(cfg, pxa.Budget.fixed(0))
+        pxa.pxa_get_workspace_layout_ex(cfg, pxa.Options.fixed(0))
     assert e.value.code == B.PXA_EINVAL
+
+
+def test_score_entry_point_validates_stride_before_launch():
+    cfg = _good()
+    _expect(B.PXA_EINVAL, pxa.pxa_proxy_score_ex, cfg, pxa.Options.dynamic(score_stride=3),
+            A, A, A, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_proxy_score_ex, cfg, pxa.Options.dynamic(score_stride=2),
+            A, None, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score_ex, cfg, None, MIS, A, A, stream=0)
 
 
 def test_budget_entry_points_validate_before_launch():
     cfg = _good()
-    _expect(B.PXA_EINVAL, pxa.pxa_budget_estimate_ex, cfg, pxa.Budget.ratio_of(0.5),
+    _expect(B.PXA_EINVAL, pxa.pxa_budget_estimate_ex, cfg, pxa.Options.ratio_of(0.5),
             A, A, A, A, A, A, ws_bytes=1 << 30, stream=0)         # ratio: no per-head budget
-    _expect(B.PXA_ENULL, pxa.pxa_budget_estimate_ex, cfg, pxa.Budget.fixed(3),
+    _expect(B.PXA_ENULL, pxa.pxa_budget_estimate_ex, cfg, pxa.Options.fixed(3),
             None, None, None, None, None, None, ws_bytes=0, stream=0)   # fixed needs k_h only
-    _expect(B.PXA_EALIGN, pxa.pxa_budget_estimate_ex, cfg, pxa.Budget.fixed(3),
+    _expect(B.PXA_EALIGN, pxa.pxa_budget_estimate_ex, cfg, pxa.Options.fixed(3),
             None, None, None, A + 2, None, None, ws_bytes=0, stream=0)
-    _expect(B.PXA_EWORKSPACE, pxa.pxa_budget_estimate_ex, cfg, pxa.Budget.dynamic(4),
-            A, A, A, A, A, A, ws_bytes=pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Budget.dynamic(4)) - 4,
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_budget_estimate_ex, cfg, pxa.Options.dynamic(4),
+            A, A, A, A, A, A, ws_bytes=pxa.pxa_budget_workspace_bytes_ex(cfg, pxa.Options.dynamic(4)) - 4,
             stream=0)
-    _expect(B.PXA_EINVAL, pxa.pxa_block_select_ex, cfg, pxa.Budget.ratio_of(0.0),
+    _expect(B.PXA_EINVAL, pxa.pxa_block_select_ex, cfg, pxa.Options.ratio_of(0.0),
             A, A, A, A, A, ws_bytes=1 << 30, stream=0)
-    _expect(B.PXA_ENULL, pxa.pxa_block_select_ex, cfg, pxa.Budget.fixed(2),
+    _expect(B.PXA_ENULL, pxa.pxa_block_select_ex, cfg, pxa.Options.fixed(2),
             A, None, A, A, A, ws_bytes=1 << 30, stream=0)          # k_h required unless ratio
-    _expect(B.PXA_EWORKSPACE, pxa.pxa_block_select_ex, cfg, pxa.Budget.ratio_of(0.5),
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_block_select_ex, cfg, pxa.Options.ratio_of(0.5),
             A, None, A, A, A, ws_bytes=pxa.pxa_select_workspace_bytes(cfg) - 4, stream=0)
-    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_ex, cfg, pxa.Budget.dynamic(4), A, A, A, A, A,
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_ex, cfg, pxa.Options.dynamic(4), A, A, A, A, A,
             ws_bytes=pxa.pxa_workspace_bytes(cfg), stream=0)     # the default size is too small
-    _expect(B.PXA_EINVAL, pxa.pxa_prefill_ex, cfg, pxa.Budget(mode=9), A, A, A, A, A,
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_ex, cfg, pxa.Options(budget_mode=9), A, A, A, A, A,
             ws_bytes=1 << 40, stream=0)
 
 

@@ -1,5 +1,6 @@
-"""GPU parity of the budget variants (probe of the last m query blocks, fixed
-budget, ratio budget) against the CPU oracle, through the C ABI.
+"""GPU parity of the method variants (budget: probe of the last m query blocks,
+fixed, ratio; scoring: the sequence-level query stride) against the CPU
+oracle, through the C ABI.
 
 Stage checks feed the kernels the oracle's own stage inputs (the GPU's scores,
 read back, for the selection); end-to-end checks run pxa_prefill_ex and compare
@@ -11,11 +12,11 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import block_sparse_long_proxy_amd as pxa  # noqa: E402
-from block_sparse_long_proxy_amd import Budget  # noqa: E402
+from block_sparse_long_proxy_amd import Options  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from parity_util import (  # noqa: E402
     host64, csr_to_keep, budget_allowed, assert_outputs_close, check_schedule, compare_masks,
-    MASS_ATOL, MASS_RTOL, MASK_AGREE)
+    MASS_ATOL, MASS_RTOL, MASK_AGREE, SCORE_RTOL)
 from test_gpu_parity import case_data, run_pool, run_score, _empty  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +39,7 @@ def test_probe_blocks_masses_and_budgets(name, m):
     wl, cfg, q, k, v, dev = case_data(name)
     m = min(m, cfg.nb)
     S_dev = run_score(cfg, *run_pool(cfg, dev))
-    budget = Budget.dynamic(m)
+    budget = Options.dynamic(m)
     kh = _empty((cfg.num_heads,), torch.int32)
     masses = _empty((cfg.num_heads, cfg.nb), torch.float32)
     ws = _empty((pxa.pxa_budget_workspace_bytes_ex(cfg, budget),), torch.uint8)
@@ -58,7 +59,7 @@ def test_probe_of_one_block_equals_the_default_budget():
     wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")
     S_dev = run_score(cfg, *run_pool(cfg, dev))
     outs = []
-    for budget in (None, Budget.dynamic(1)):
+    for budget in (None, Options.dynamic(1)):
         kh = _empty((cfg.num_heads,), torch.int32)
         masses = _empty((cfg.num_heads, cfg.nb), torch.float32)
         ws = _empty((pxa.pxa_budget_workspace_bytes_ex(cfg, budget),), torch.uint8)
@@ -74,7 +75,7 @@ def test_fixed_budget_selection_exact(name):
     S_dev = run_score(cfg, *run_pool(cfg, dev))
     S = host64(S_dev)
     for kk in sorted({1, 3, cfg.nb}):
-        budget = Budget.fixed(kk)
+        budget = Options.fixed(kk)
         kh = torch.full((cfg.num_heads,), -5, dtype=torch.int32, device="cuda")
         pxa.pxa_budget_estimate_ex(cfg, budget, None, None, None, kh, None, None)
         assert np.all(kh.cpu().numpy() == kk)
@@ -91,7 +92,7 @@ def test_ratio_selection_exact(name):
     S_dev = run_score(cfg, *run_pool(cfg, dev))
     S = host64(S_dev)
     for r in (0.05, 0.3, 0.5, 1.0):
-        rp, ci, order = _select_ex(cfg, Budget.ratio_of(r), S_dev, None)   # k_h unused
+        rp, ci, order = _select_ex(cfg, Options.ratio_of(r), S_dev, None)   # k_h unused
         check_schedule(order, rp)
         keep_ref = O.select_blocks_ratio(S, r, cfg.num_heads)
         np.testing.assert_array_equal(csr_to_keep(rp, ci, cfg.num_heads, cfg.nb), keep_ref,
@@ -103,7 +104,7 @@ def test_ratio_count_float32_tie():
     # must round to nearest-even (3.0) before the ceiling, as the oracle does.
     wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")   # nb = 13 > 9
     S_dev = run_score(cfg, *run_pool(cfg, dev))
-    rp, ci, _ = _select_ex(cfg, Budget.ratio_of(0.3), S_dev, None)
+    rp, ci, _ = _select_ex(cfg, Options.ratio_of(0.3), S_dev, None)
     lens = np.diff(rp).reshape(cfg.num_heads, cfg.nb)
     S = host64(S_dev)
     for h in range(cfg.num_heads):
@@ -115,7 +116,7 @@ def test_ratio_count_float32_tie():
 
 
 @pytest.mark.parametrize("name", ["c0", "G1_7heads"])
-@pytest.mark.parametrize("budget", [Budget.dynamic(3), Budget.fixed(2), Budget.ratio_of(0.25)],
+@pytest.mark.parametrize("budget", [Options.dynamic(3), Options.fixed(2), Options.ratio_of(0.25)],
                          ids=["dynamic3", "fixed2", "ratio0.25"])
 def test_prefill_ex_end_to_end(name, budget):
     wl, cfg, q, k, v, dev = case_data(name)
@@ -128,7 +129,7 @@ def test_prefill_ex_end_to_end(name, budget):
     keep_gpu = csr_to_keep(rp, ci, H, nb)
     check_schedule(attn.row_order.cpu().numpy(), rp)
     mode = {pxa.PXA_BUDGET_DYNAMIC: "dynamic", pxa.PXA_BUDGET_FIXED: "fixed",
-            pxa.PXA_BUDGET_RATIO: "ratio"}[budget.mode]
+            pxa.PXA_BUDGET_RATIO: "ratio"}[budget.budget_mode]
     spec = {"mode": mode, "last_blocks": budget.last_blocks, "blocks": budget.fixed_blocks,
             "ratio": budget.ratio}
     ref = O.pipeline(q, k, v, cfg.num_proxies, wl.gamma, budget=spec, with_output=False)
@@ -149,3 +150,39 @@ def test_prefill_ex_end_to_end(name, budget):
     # outputs on the GPU's own mask
     o_ref = O.sparse_attention(q, k, v, keep_gpu, 128, cfg.scale)
     assert_outputs_close(o.float().cpu().numpy().astype(np.float64), o_ref, f"{name} {mode}")
+
+
+@pytest.mark.parametrize("name", NAMES + ["single_block"])
+@pytest.mark.parametrize("stride", [2, 4])
+def test_strided_scores_parity(name, stride):
+    wl, cfg, q, k, v, dev = case_data(name)
+    qb, kb = run_pool(cfg, dev)
+    S_dev = _empty((cfg.num_proxies, cfg.nb, cfg.nb), torch.float32)
+    pxa.pxa_proxy_score_ex(cfg, Options.dynamic(score_stride=stride), qb, kb, S_dev)
+    got = host64(S_dev)
+    ref = O.proxy_scores(host64(qb), host64(kb), 128, cfg.scale, query_stride=stride)
+    fin = np.isfinite(ref)
+    np.testing.assert_array_equal(np.isfinite(got), fin)
+    assert np.all(np.isneginf(got[~fin]))
+    err = np.abs(got[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), 1.0)
+    assert err.max() <= SCORE_RTOL, err.max()
+    full = host64(run_score(cfg, qb, kb))
+    assert np.all(got[fin] <= full[fin] + 1e-6 * np.maximum(np.abs(full[fin]), 1.0))
+
+
+@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+def test_prefill_ex_with_query_stride(name):
+    wl, cfg, q, k, v, dev = case_data(name)
+    opts = Options.dynamic(score_stride=2)
+    attn = pxa.ProxyAttn(cfg, opts)
+    o = attn(dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    H, nb = cfg.num_heads, cfg.nb
+    rp = attn.row_ptr.cpu().numpy()
+    keep_gpu = csr_to_keep(rp, attn.col_idx[: int(rp[-1])].cpu().numpy(), H, nb)
+    ref = O.pipeline(q, k, v, cfg.num_proxies, wl.gamma, with_output=False, score_stride=2)
+    frac, rep = compare_masks(keep_gpu, ref["S"], ref["k_h"], attn.k_h.cpu().numpy(),
+                              ref["masses"], cfg.num_proxies, wl.gamma)
+    assert frac >= MASK_AGREE and not rep["bad"], (frac, rep["bad"][:5])
+    o_ref = O.sparse_attention(q, k, v, keep_gpu, 128, cfg.scale)
+    assert_outputs_close(o.float().cpu().numpy().astype(np.float64), o_ref, f"{name} stride 2")

@@ -1,4 +1,4 @@
-"""Budget variants at a full workload size (32K tokens, one proxy), run as the
+"""Options variants at a full workload size (32K tokens, one proxy), run as the
 benchmark runs them (pxa_prefill_ex): the probe masses of every head against
 the oracle, and the size-independent properties of each variant's mask."""
 import numpy as np
@@ -35,7 +35,7 @@ def _run(cfg, dev, budget):
 def test_probe_of_four_blocks(data):
     wl, cfg, x, dev = data
     m = 4
-    attn, rp, ci = _run(cfg, dev, pxa.Budget.dynamic(m))
+    attn, rp, ci = _run(cfg, dev, pxa.Options.dynamic(m))
     H, Hkv, G, nb = cfg.num_heads, cfg.num_kv_heads, cfg.num_proxies, cfg.nb
     S = attn.scores.cpu().numpy().astype(np.float64)
     masses, kh = attn.masses.cpu().numpy().astype(np.float64), attn.k_h.cpu().numpy()
@@ -54,8 +54,8 @@ def test_probe_of_four_blocks(data):
 
 
 @pytest.mark.parametrize("budget,count", [
-    (pxa.Budget.fixed(16), lambda I: min(16, I + 1)),
-    (pxa.Budget.ratio_of(0.1), lambda I: O.ratio_count(I, 0.1)),
+    (pxa.Options.fixed(16), lambda I: min(16, I + 1)),
+    (pxa.Options.ratio_of(0.1), lambda I: O.ratio_count(I, 0.1)),
 ], ids=["fixed16", "ratio0.1"])
 def test_fixed_and_ratio_masks(data, budget, count):
     wl, cfg, x, dev = data
