@@ -16,7 +16,8 @@ it, in the order of its section 4 ("ProxyAttn方法详解"):
                                  probe of several blocks), budget_from_masses
   budget variants             -> fixed k per head; ratio_count, select_blocks_ratio
   final sparse mask           -> select_blocks
-  FlashAttention on the mask  -> sparse_attention
+  FlashAttention on the mask  -> sparse_attention (sparse_attention_row_skip:
+                                 BLASST's running-max skip, an approximation)
 
 Readings taken where the pages leave a step open (each is stated again in the
 function that applies it):
@@ -342,6 +343,55 @@ def sparse_attention_row(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
     P = np.exp(L)
     P /= P.sum(axis=1, keepdims=True)
     return P @ np.asarray(v_kv[cols], dtype=np.float64)
+
+
+def sparse_attention_row_skip(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
+                              blocks: Sequence[int], I: int, block: int, scale: float,
+                              threshold: float, group: int = 32):
+    """Output rows of query block I with BLASST's running-max skip.
+
+    BLASST (the translated BLASST paper, introduction and method): blocks are
+    processed in sequence with a running maximum of the attention scores; a
+    block whose local maximum lies so far below the running maximum that its
+    normalised weights are negligible is skipped (no exponentials, no P.V).
+    Readings: the kept blocks are visited in descending order (the diagonal
+    block first, as the GPU kernel visits them); the threshold lam in (0, 1]
+    applies to the weight ratio, so a block is skipped when
+    exp(local max - running max) < lam (scaled logits); the decision is taken
+    for `group` consecutive queries together (all of them must satisfy it);
+    a skipped block leaves the running state untouched.
+
+    Returns (out [B, d] float64, skipped: list of (block J, group index)).
+    """
+    q64 = np.asarray(q_h[I * block:(I + 1) * block], dtype=np.float64)
+    k64 = np.asarray(k_kv, dtype=np.float64)
+    v64 = np.asarray(v_kv, dtype=np.float64)
+    d = v64.shape[1]
+    qi = np.arange(I * block, (I + 1) * block)
+    m = np.full(block, NEG_INF)
+    lsum = np.zeros(block)
+    acc = np.zeros((block, d))
+    skipped = []
+    log_thr = math.log(threshold)
+    for J in sorted((int(b) for b in blocks if 0 <= b <= I), reverse=True):
+        cols = np.arange(J * block, (J + 1) * block)
+        L = scale * (q64 @ k64[cols].T)
+        L = np.where(cols[None, :] <= qi[:, None], L, NEG_INF)
+        tmax = L.max(axis=1)
+        for gi in range(block // group):
+            rows = slice(gi * group, (gi + 1) * group)
+            mg, tg = m[rows], tmax[rows]
+            if np.all(np.isfinite(mg)) and np.all(tg - mg < log_thr):
+                skipped.append((J, gi))
+                continue
+            m_new = np.maximum(mg, tg)
+            alpha = np.where(np.isfinite(mg), np.exp(mg - m_new), 0.0)
+            P = np.exp(L[rows] - m_new[:, None])
+            lsum[rows] = lsum[rows] * alpha + P.sum(axis=1)
+            acc[rows] = acc[rows] * alpha[:, None] + P @ v64[cols]
+            m[rows] = m_new
+    out = np.where(lsum[:, None] > 0, acc / np.where(lsum > 0, lsum, 1.0)[:, None], 0.0)
+    return out, skipped
 
 
 def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,

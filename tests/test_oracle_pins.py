@@ -461,3 +461,58 @@ def test_strided_scores_bound_and_stride_one():
 def test_strided_scores_reject_bad_stride():
     with pytest.raises(ValueError):
         O.proxy_score_row(np.zeros((32, 2)), np.zeros((32, 2)), 0, 16, 1.0, query_stride=3)
+
+
+# ---------------------------------------------------------------- running-max skip (BLASST)
+def test_skip_with_negligible_threshold_is_plain_attention():
+    N, d, B = 64, 4, 16
+    q, k, v = _rand((N, d), 70, 2.0), _rand((N, d), 71), _rand((N, d), 72)
+    blocks = [0, 2, 3]
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, 3, B, 0.5, 1e-300, group=8)
+    assert skipped == []
+    np.testing.assert_allclose(out, O.sparse_attention_row(q, k, v, blocks, 3, B, 0.5), rtol=1e-12, atol=1e-14)
+
+
+def test_skip_bruteforce_decisions_and_output():
+    # pure-Python online softmax over descending blocks with per-group decisions
+    N, d, B, G = 48, 3, 16, 4
+    q, k, v = _rand((N, d), 73, 2.5), _rand((N, d), 74, 1.5), _rand((N, d), 75)
+    I, blocks, lam, scale = 2, [0, 1, 2], 0.5, 3.0
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam, group=G)
+    m = [-math.inf] * B
+    l = [0.0] * B
+    acc = [[0.0] * d for _ in range(B)]
+    want_skip = []
+    for J in (2, 1, 0):
+        logits = [[(scale * sum(q[I * B + i][c] * k[J * B + j][c] for c in range(d))
+                    if J * B + j <= I * B + i else -math.inf) for j in range(B)] for i in range(B)]
+        for gi in range(B // G):
+            rows = range(gi * G, (gi + 1) * G)
+            if all(m[i] > -math.inf and math.exp(max(logits[i]) - m[i]) < lam for i in rows):
+                want_skip.append((J, gi))
+                continue
+            for i in rows:
+                mn = max(m[i], max(logits[i]))
+                a = math.exp(m[i] - mn) if m[i] > -math.inf else 0.0
+                w = [math.exp(x - mn) if x > -math.inf else 0.0 for x in logits[i]]
+                l[i] = l[i] * a + math.fsum(w)
+                for c in range(d):
+                    acc[i][c] = acc[i][c] * a + math.fsum(w[j] * v[J * B + j][c] for j in range(B))
+                m[i] = mn
+    assert skipped == want_skip and len(want_skip) > 0
+    np.testing.assert_allclose(out, np.array(acc) / np.array(l)[:, None], rtol=1e-12, atol=1e-14)
+
+
+def test_skip_set_grows_with_threshold_and_error_is_bounded():
+    N, d, B = 128, 8, 16
+    q, k, v = _rand((N, d), 76, 3.0), _rand((N, d), 77, 1.5), _rand((N, d), 78)
+    I, blocks = 7, list(range(8))
+    exact = O.sparse_attention_row(q, k, v, blocks, I, B, 0.5)
+    prev = set()
+    for lam in (1e-6, 1e-4, 1e-2, 1e-1):
+        out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, 0.5, lam, group=4)
+        assert prev <= set(skipped)
+        prev = set(skipped)
+        # a skipped block holds at most 16 keys of weight < lam * max weight each
+        assert np.max(np.abs(out - exact)) <= 2 * 16 * len(blocks) * lam * np.abs(v).max() + 1e-12
+    assert prev                                             # something was skipped at 0.1
