@@ -11,7 +11,8 @@ include/pxa.h); this package only marshals torch tensors to it.
     attn.k_h, attn.row_ptr, attn.col_idx, attn.scores   # the mask it used
 
 Method variants: ProxyAttn(cfg, Options.dynamic(last_blocks=4)),
-Options.fixed(blocks=64), Options.ratio_of(0.1), Options.dynamic(score_stride=2).
+Options.fixed(blocks=64), Options.ratio_of(0.1), Options.dynamic(score_stride=2),
+Options.dynamic(skip_threshold=1e-3) (BLASST's running-max skip in the attention).
 """
 from ._binding import (  # noqa: F401
     Config, PxaError, load_library, LIB_PATH,
@@ -22,6 +23,7 @@ from ._binding import (  # noqa: F401
     Options, PXA_BUDGET_DYNAMIC, PXA_BUDGET_FIXED, PXA_BUDGET_RATIO, PXA_MAX_PROBE_BLOCKS,
     pxa_validate_options, pxa_proxy_score_ex, pxa_workspace_bytes_ex, pxa_get_workspace_layout_ex,
     pxa_budget_workspace_bytes_ex, pxa_prefill_ex, pxa_budget_estimate_ex, pxa_block_select_ex,
+    pxa_sparse_prefill_ex, pxa_dense_prefill_ex,
 )
 
 

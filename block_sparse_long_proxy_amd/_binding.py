@@ -50,7 +50,7 @@ PXA_MAX_PROBE_BLOCKS = 64
 class pxa_options(ctypes.Structure):
     _fields_ = [("budget_mode", ctypes.c_int32), ("last_blocks", ctypes.c_int32),
                 ("fixed_blocks", ctypes.c_int32), ("ratio", ctypes.c_float),
-                ("score_stride", ctypes.c_int32)]
+                ("score_stride", ctypes.c_int32), ("skip_threshold", ctypes.c_float)]
 
 
 class pxa_workspace_layout(ctypes.Structure):
@@ -81,6 +81,8 @@ _SIGNATURES = {
     "pxa_dense_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
     "pxa_validate_options": (ctypes.c_int, [_CFG, _OPT]),
     "pxa_proxy_score_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P]),
+    "pxa_sparse_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pxa_dense_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P]),
     "pxa_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
     "pxa_get_workspace_layout_ex": (ctypes.c_int, [_CFG, _OPT, ctypes.POINTER(pxa_workspace_layout)]),
     "pxa_budget_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
@@ -143,22 +145,26 @@ class Options:
     fixed_blocks: int = 0
     ratio: float = 0.0
     score_stride: int = 1
+    skip_threshold: float = 0.0
 
     @staticmethod
-    def dynamic(last_blocks: int = 1, score_stride: int = 1) -> "Options":
-        return Options(PXA_BUDGET_DYNAMIC, last_blocks=last_blocks, score_stride=score_stride)
+    def dynamic(last_blocks: int = 1, score_stride: int = 1, skip_threshold: float = 0.0) -> "Options":
+        return Options(PXA_BUDGET_DYNAMIC, last_blocks=last_blocks, score_stride=score_stride,
+                       skip_threshold=skip_threshold)
 
     @staticmethod
-    def fixed(blocks: int, score_stride: int = 1) -> "Options":
-        return Options(PXA_BUDGET_FIXED, fixed_blocks=blocks, score_stride=score_stride)
+    def fixed(blocks: int, score_stride: int = 1, skip_threshold: float = 0.0) -> "Options":
+        return Options(PXA_BUDGET_FIXED, fixed_blocks=blocks, score_stride=score_stride,
+                       skip_threshold=skip_threshold)
 
     @staticmethod
-    def ratio_of(r: float, score_stride: int = 1) -> "Options":
-        return Options(PXA_BUDGET_RATIO, ratio=r, score_stride=score_stride)
+    def ratio_of(r: float, score_stride: int = 1, skip_threshold: float = 0.0) -> "Options":
+        return Options(PXA_BUDGET_RATIO, ratio=r, score_stride=score_stride,
+                       skip_threshold=skip_threshold)
 
     def c(self) -> pxa_options:
         return pxa_options(self.budget_mode, self.last_blocks, self.fixed_blocks, self.ratio,
-                           self.score_stride)
+                           self.score_stride, self.skip_threshold)
 
 
 def _bref(opts: Optional[Options]):
@@ -358,3 +364,18 @@ def pxa_block_select_ex(cfg: Config, opts: Optional[Options], scores, k_h, row_p
         _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
         _tp(row_order, "i32", "row_order"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
         _stream(stream)), "pxa_block_select_ex")
+
+
+def pxa_sparse_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, row_ptr, col_idx, o,
+                          stream=None, row_order=None) -> None:
+    _check(load_library().pxa_sparse_prefill_ex(
+        ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
+        _tp(v, "bf16", "v"), _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
+        _tp(row_order, "i32", "row_order"), _tp(o, "bf16", "o"), _stream(stream)),
+        "pxa_sparse_prefill_ex")
+
+
+def pxa_dense_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, stream=None) -> None:
+    _check(load_library().pxa_dense_prefill_ex(
+        ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
+        _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill_ex")

@@ -14,6 +14,8 @@
 // copy of the next tile is issued before the MFMA phase it hides behind (V
 // during S + softmax, the next K during PV).  V stays row-major in LDS and is
 // read transposed with ds_read_b64_tr_b16.
+#include <cmath>
+
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -23,16 +25,20 @@ namespace pxa {
 // (S^T layout: this lane's query, 64 of the tile's keys).  Masked entries are
 // -inf.  Returns the bf16 probabilities in the B-operand layout of the PV
 // MFMA and rescales the running output when the running max moved.
-template <int D>
-__device__ __forceinline__ void softmax_update(f32x16 (&s)[4], bf16x8 (&pb)[4][2],
-                                               f32x16 (&oacc)[D / 32], float& m_run,
-                                               float& l_run, float scale_log2) {
+// Row max of a tile (this lane's 64 logits, then the lane holding the same query).
+__device__ __forceinline__ float tile_row_max(const f32x16 (&s)[4]) {
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  return fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+template <int D>
+__device__ __forceinline__ void softmax_update(f32x16 (&s)[4], float mx, bf16x8 (&pb)[4][2],
+                                               f32x16 (&oacc)[D / 32], float& m_run,
+                                               float& l_run, float scale_log2) {
   const float m_new = fmaxf(m_run, mx);
   // m_new is finite once any unmasked key has been seen (always true after
   // the diagonal block, which comes first when present).
@@ -70,12 +76,15 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], bf16x8 (&pb)[4][2
 
 // One pipeline step on key block J (tiles already in LDS / landing): S, the
 // softmax, then O += V P, issuing the copies of block Jn (< 0: none).
+// skip_delta (raw logit units, -inf: off): the running-max skip of the
+// BLASST pages -- when every query of the wave has its tile max below
+// m_run + skip_delta, the wave drops the tile's softmax and PV product.
 template <int D, bool DIAG>
 __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_lds, __bf16* ks,
                                         __bf16* vs, const bf16x8 (&qf)[D / 16],
                                         f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
                                         float scale_log2, int qloc, const __bf16* knext,
-                                        const __bf16* vnext) {
+                                        const __bf16* vnext, float skip_delta) {
   f32x16 s[4];
   // S^T = K Q^T with the four K fragments of k-step ss+1 read while the four
   // products of step ss issue (scheduling barriers keep that order).
@@ -106,19 +115,24 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
         if (acc_key(t, r) > qloc) s[t][r] = -INFINITY;
   }
   bf16x8 pb[4][2];
-  softmax_update<D>(s, pb, oacc, m_run, l_run, scale_log2);
+  const float mx = tile_row_max(s);
+  // m_run is -inf only before the first tile, where the comparison is false
+  const bool skip = !DIAG && __all(mx < m_run + skip_delta);
+  if (!skip) softmax_update<D>(s, mx, pb, oacc, m_run, l_run, scale_log2);
 
   wait_vmem();                   // this thread's part of V(J) has landed
   __syncthreads();               // V(J) visible; every wave is done with the K tile
   if (knext) tile_load_lds<D, false>(knext, ks);
 
+  if (!skip) {
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-      for (int m = 0; m < D / 32; ++m)
-        oacc[m] = mfma32(vfrag_tr<D>(vs_lds, m, t, s2), pb[t][s2], oacc[m]);
+        for (int m = 0; m < D / 32; ++m)
+          oacc[m] = mfma32(vfrag_tr<D>(vs_lds, m, t, s2), pb[t][s2], oacc[m]);
+  }
 
   wait_vmem();                   // this thread's part of K(Jn) has landed
   __syncthreads();               // K(Jn) visible; every wave is done with the V tile
@@ -130,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
     const int32_t* __restrict__ row_order, __bf16* __restrict__ o, int H, int Hkv, int N,
-    float scale_log2) {
+    float scale_log2, float skip_delta) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];   // K tile, kswz layout
   __shared__ __attribute__((aligned(16))) __bf16 vs[kBlock * D];   // V tile, vswz layout
 
@@ -215,7 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int Jn = next_block(it);
     fa_step<D, true>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                      Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
-                     Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr);
+                     Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr, skip_delta);
     J = Jn;
   }
   while (J >= 0) {
@@ -223,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int Jn = next_block(it);
     fa_step<D, false>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                       Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
-                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr);
+                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr, skip_delta);
     J = Jn;
   }
 
@@ -249,14 +263,16 @@ static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, c
                             const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
   const dim3 grid(a.H * (a.N / kBlock)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
+  // skip when scale * (tile max - running max) < ln(threshold)
+  const float skip_delta = a.skip_threshold > 0.f ? std::log(a.skip_threshold) / a.scale : -INFINITY;
   if (dense)
     hipLaunchKernelGGL((fa_prefill_kernel<D, true>), grid, block, 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2, skip_delta);
   else
     hipLaunchKernelGGL((fa_prefill_kernel<D, false>), grid, block, 0, stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2);
+                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2, skip_delta);
   return hipGetLastError();
 }
 

@@ -44,6 +44,8 @@ int check_budget(const pxa_config* c, const pxa_options* b) {
   if (!b) return PXA_OK;
   const int nb = c->seq_len / pxa::kBlockTokens;
   if (b->score_stride != 1 && b->score_stride != 2 && b->score_stride != 4) return PXA_EINVAL;
+  if (!std::isfinite(b->skip_threshold) || b->skip_threshold < 0.f || b->skip_threshold > 1.f)
+    return PXA_EINVAL;
   switch (b->budget_mode) {
     case PXA_BUDGET_DYNAMIC:
       if (b->last_blocks < 1 || b->last_blocks > nb || b->last_blocks > PXA_MAX_PROBE_BLOCKS)
@@ -78,6 +80,7 @@ pxa::LaunchArgs args_of(const pxa_config* c, const pxa_options* b = nullptr) {
     a.fixed_blocks = b->fixed_blocks;
     a.ratio = b->ratio;
     a.score_stride = b->score_stride;
+    a.skip_threshold = b->skip_threshold;
   }
   return a;
 }
@@ -274,24 +277,36 @@ int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* 
                              stream);
 }
 
-int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
-                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_order,
-                       void* o, void* stream) {
-  int rc = check_config(cfg);
+int pxa_sparse_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                          const void* k, const void* v, const int32_t* row_ptr,
+                          const int32_t* col_idx, const int32_t* row_order, void* o,
+                          void* stream) {
+  int rc = check_all(cfg, opts);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {row_ptr, 4}, {col_idx, 4}, {o, 16}}))) return rc;
   if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, row_ptr, col_idx, row_order, o,
-                                       false, (hipStream_t)stream));
+  return hip_rc(pxa::launch_fa_prefill(args_of(cfg, opts), q, k, v, row_ptr, col_idx, row_order,
+                                       o, false, (hipStream_t)stream));
+}
+
+int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
+                       const int32_t* row_ptr, const int32_t* col_idx, const int32_t* row_order,
+                       void* o, void* stream) {
+  return pxa_sparse_prefill_ex(cfg, nullptr, q, k, v, row_ptr, col_idx, row_order, o, stream);
+}
+
+int pxa_dense_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                         const void* k, const void* v, void* o, void* stream) {
+  int rc = check_all(cfg, opts);
+  if (rc) return rc;
+  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}}))) return rc;
+  return hip_rc(pxa::launch_fa_prefill(args_of(cfg, opts), q, k, v, nullptr, nullptr, nullptr, o,
+                                       true, (hipStream_t)stream));
 }
 
 int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
                       void* stream) {
-  int rc = check_config(cfg);
-  if (rc) return rc;
-  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}}))) return rc;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg), q, k, v, nullptr, nullptr, nullptr, o,
-                                       true, (hipStream_t)stream));
+  return pxa_dense_prefill_ex(cfg, nullptr, q, k, v, o, stream);
 }
 
 int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* budget, const void* q,

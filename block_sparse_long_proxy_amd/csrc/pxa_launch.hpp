@@ -20,6 +20,7 @@ struct LaunchArgs {
   int fixed_blocks = 0;   // fixed budget: blocks per row
   float ratio = 0.f;      // ratio budget
   int score_stride = 1;   // queries scored per block: 128 / score_stride
+  float skip_threshold = 0.f;   // running-max skip of the attention (0: off)
 };
 
 hipError_t launch_proxy_pool(const LaunchArgs& a, const void* q, const void* k, void* qbar,

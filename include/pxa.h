@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 3
+#define PXA_ABI_VERSION 4
 
 enum {
   PXA_OK = 0,
@@ -79,7 +79,10 @@ typedef struct pxa_config {
  * read as scoring only every s-th query of a block (offsets s-1, 2s-1, ...,
  * B-1) against every key -- an approximation of the s = 1 scores.  Every
  * entry point that takes a `const pxa_options*` reads NULL as
- * {PXA_BUDGET_DYNAMIC, 1, 0, 0, 1}, the behaviour of the calls without _ex. */
+ * {PXA_BUDGET_DYNAMIC, 1, 0, 0, 1, 0}, the behaviour of the calls without _ex.
+ * Attention: skip_threshold > 0 turns on the running-max skip of the BLASST
+ * pages (kept blocks are visited diagonal first, then by descending index; a
+ * skipped block costs its QK^T product only). */
 enum { PXA_BUDGET_DYNAMIC = 0, PXA_BUDGET_FIXED = 1, PXA_BUDGET_RATIO = 2 };
 #define PXA_MAX_PROBE_BLOCKS 64
 typedef struct pxa_options {
@@ -92,6 +95,10 @@ typedef struct pxa_options {
                             blocks (product rounded to fp32 first; at least 1)
                             plus the diagonal, the same for every head           */
   int32_t score_stride;  /* 1, 2 or 4: queries scored per block = B / stride     */
+  float skip_threshold;  /* 0: off.  0 < lam <= 1: BLASST running-max skip in the
+                            attention (a 32-query group skips a block when
+                            exp(block max - running max) < lam for all its
+                            queries, scaled logits) -- an approximation          */
 } pxa_options;
 
 /* Sizes and offsets of the whole-pipeline workspace (bytes from its start).
@@ -228,11 +235,19 @@ int pxa_block_select_ex(const pxa_config* cfg, const pxa_options* opts, const fl
 int pxa_sparse_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
                        const int32_t* row_ptr, const int32_t* col_idx,
                        const int32_t* row_order, void* o, void* stream);
+/* The same with opts->skip_threshold (other fields are not used). */
+int pxa_sparse_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                          const void* k, const void* v, const int32_t* row_ptr,
+                          const int32_t* col_idx, const int32_t* row_order, void* o,
+                          void* stream);
 
 /* Dense causal attention with the same kernel (every block J <= I kept):
  * the baseline the sparse path is measured against. */
 int pxa_dense_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v,
                       void* o, void* stream);
+/* Dense causal attention with the running-max skip (BLASST on its own). */
+int pxa_dense_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                         const void* k, const void* v, void* o, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,13 +33,13 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 3
+    assert pxa.pxa_abi_version() == 4
 
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.pxa_config) == 32
     assert ctypes.sizeof(B.pxa_workspace_layout) == 11 * ctypes.sizeof(ctypes.c_size_t)
-    assert ctypes.sizeof(B.pxa_options) == 20
+    assert ctypes.sizeof(B.pxa_options) == 24
     with open(os.path.join(ROOT, "include", "pxa.h")) as f:
         hdr = f.read()
     for name, val in (("PXA_BUDGET_DYNAMIC", 0), ("PXA_BUDGET_FIXED", 1), ("PXA_BUDGET_RATIO", 2)):
@@ -70,6 +70,11 @@ def test_struct_layouts_match_header():
     (pxa.Options.dynamic(score_stride=3), B.PXA_EINVAL),
     (pxa.Options.dynamic(score_stride=8), B.PXA_EINVAL),
     (pxa.Options.fixed(2, score_stride=0), B.PXA_EINVAL),
+    (pxa.Options.dynamic(skip_threshold=1e-3), B.PXA_OK),
+    (pxa.Options.dynamic(skip_threshold=1.0), B.PXA_OK),
+    (pxa.Options.dynamic(skip_threshold=-0.1), B.PXA_EINVAL),
+    (pxa.Options.dynamic(skip_threshold=1.5), B.PXA_EINVAL),
+    (pxa.Options.dynamic(skip_threshold=float("nan")), B.PXA_EINVAL),
 ])
 def test_validate_budget_codes(budget, code):
     assert pxa.pxa_validate_options(_good(), budget) == code
@@ -106,6 +111,16 @@ def test_score_entry_point_validates_stride_before_launch():
     _expect(B.PXA_ENULL, pxa.pxa_proxy_score_ex, cfg, pxa.Options.dynamic(score_stride=2),
             A, None, A, stream=0)
     _expect(B.PXA_EALIGN, pxa.pxa_proxy_score_ex, cfg, None, MIS, A, A, stream=0)
+
+
+def test_attention_entry_points_validate_options_before_launch():
+    cfg = _good()
+    _expect(B.PXA_EINVAL, pxa.pxa_sparse_prefill_ex, cfg, pxa.Options.dynamic(skip_threshold=2.0),
+            A, A, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_dense_prefill_ex, cfg, pxa.Options.dynamic(skip_threshold=-1.0),
+            A, A, A, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_dense_prefill_ex, cfg, None, MIS, A, A, A, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_sparse_prefill_ex, cfg, None, A, A, A, None, A, A, stream=0)
 
 
 def test_budget_entry_points_validate_before_launch():

@@ -186,3 +186,77 @@ def test_prefill_ex_with_query_stride(name):
     assert frac >= MASK_AGREE and not rep["bad"], (frac, rep["bad"][:5])
     o_ref = O.sparse_attention(q, k, v, keep_gpu, 128, cfg.scale)
     assert_outputs_close(o.float().cpu().numpy().astype(np.float64), o_ref, f"{name} stride 2")
+
+
+# ---------------------------------------------------------------- running-max skip (BLASST)
+def _mask_of(cfg, dev):
+    attn = pxa.ProxyAttn(cfg)
+    attn(dev["q"], dev["k"], dev["v"])
+    torch.cuda.synchronize()
+    rp = attn.row_ptr.clone()
+    return attn, rp, attn.col_idx.clone(), attn.row_order.clone()
+
+
+@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+def test_skip_with_negligible_threshold_is_bit_identical(name):
+    wl, cfg, q, k, v, dev = case_data(name)
+    attn, rp, ci, order = _mask_of(cfg, dev)
+    o0, o1 = torch.empty_like(dev["q"]), torch.empty_like(dev["q"])
+    pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], rp, ci, o0, row_order=order)
+    pxa.pxa_sparse_prefill_ex(cfg, Options.dynamic(skip_threshold=1e-30), dev["q"], dev["k"],
+                              dev["v"], rp, ci, o1, row_order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
+
+
+def _robust_skip_rows(q, k, v, cfg, kv_of, rows_blocks, lam):
+    """Oracle outputs of the rows whose skip decisions do not move when lam
+    moves by 0.1% either way (a decision on the threshold may go either way
+    in fp32 on the GPU)."""
+    out = {}
+    for (h, I), blocks in rows_blocks.items():
+        kv = kv_of(h)
+        res = [O.sparse_attention_row_skip(q[h], k[kv], v[kv], blocks, I, 128, cfg.scale, x)
+               for x in (lam * 0.999, lam, min(1.0, lam * 1.001))]
+        if res[0][1] == res[1][1] == res[2][1]:
+            out[(h, I)] = res[1]
+    return out
+
+
+@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+@pytest.mark.parametrize("lam", [1e-3, 0.05, 1.0])
+def test_sparse_skip_parity(name, lam):
+    wl, cfg, q, k, v, dev = case_data(name)
+    attn, rp, ci, order = _mask_of(cfg, dev)
+    o = torch.empty_like(dev["q"])
+    pxa.pxa_sparse_prefill_ex(cfg, Options.dynamic(skip_threshold=lam), dev["q"], dev["k"],
+                              dev["v"], rp, ci, o, row_order=order)
+    torch.cuda.synchronize()
+    H, Hkv, nb = cfg.num_heads, cfg.num_kv_heads, cfg.nb
+    rp_h, ci_h, o_h = rp.cpu().numpy(), ci.cpu().numpy(), o.float().cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(9)
+    rows = {(h, I): ci_h[rp_h[h * nb + I]:rp_h[h * nb + I + 1]]
+            for h in range(H) for I in sorted({nb - 1, nb // 2, *rng.integers(0, nb, 3).tolist()})}
+    ref = _robust_skip_rows(q, k, v, cfg, lambda h: O.kv_head_of(h, H, Hkv), rows, lam)
+    assert len(ref) >= 0.8 * len(rows), (len(ref), len(rows))
+    n_skipped = 0
+    for (h, I), (out, skipped) in ref.items():
+        n_skipped += len(skipped)
+        assert_outputs_close(o_h[h, I * 128:(I + 1) * 128], out, f"{name} h{h} I{I} lam {lam}")
+    if lam == 1.0:
+        assert n_skipped > 0                        # the rule did act on these inputs
+
+
+def test_dense_skip_parity():
+    wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")
+    lam = 0.02
+    o = torch.empty_like(dev["q"])
+    pxa.pxa_dense_prefill_ex(cfg, Options.dynamic(skip_threshold=lam), dev["q"], dev["k"], dev["v"], o)
+    torch.cuda.synchronize()
+    H, Hkv, nb = cfg.num_heads, cfg.num_kv_heads, cfg.nb
+    o_h = o.float().cpu().numpy().astype(np.float64)
+    rows = {(h, I): np.arange(I + 1) for h in (0, 3, 6) for I in (nb - 1, nb // 2, 1)}
+    ref = _robust_skip_rows(q, k, v, cfg, lambda h: O.kv_head_of(h, H, Hkv), rows, lam)
+    assert len(ref) >= 0.8 * len(rows)
+    for (h, I), (out, skipped) in ref.items():
+        assert_outputs_close(o_h[h, I * 128:(I + 1) * 128], out, f"dense h{h} I{I}")
