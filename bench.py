@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--score-stride", type=int, default=1,
                     help="sequence-level skip of the proxy scoring: score every s-th query "
                          "(1, 2 or 4; 1 = every query, the default)")
+    ap.add_argument("--skip-threshold", type=float, default=0.0,
+                    help="BLASST running-max skip inside the attention (0 = off, the default)")
     ap.add_argument("--budget", default="dynamic:1",
                     help="budget variant: dynamic:M (probe the last M query blocks; the method's "
                          "own budget, M=1 by default), fixed:K or ratio:R")
@@ -208,7 +210,8 @@ def main():
               "fixed": lambda: pxa.Options.fixed(int(val)),
               "ratio": lambda: pxa.Options.ratio_of(float(val))}[kind]()
     import dataclasses
-    budget = dataclasses.replace(budget, score_stride=a.score_stride)
+    budget = dataclasses.replace(budget, score_stride=a.score_stride,
+                                 skip_threshold=a.skip_threshold)
     budget_desc = {"mode": kind, **({"last_blocks": budget.last_blocks} if kind == "dynamic" else
                                     {"blocks": budget.fixed_blocks} if kind == "fixed" else
                                     {"ratio": budget.ratio})}
@@ -239,7 +242,7 @@ def main():
             pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.scores)
             budget_stage()
             select_stage()
-            pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
+            pxa.pxa_sparse_prefill_ex(cfg, budget, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
                                    row_order=attn.row_order)
         torch.cuda.synchronize()
         log(f"profile pass done: kept blocks {int(attn.row_ptr[-1])}")
@@ -277,7 +280,7 @@ def main():
         evs[3].record(stream)
         select_stage()
         evs[4].record(stream)
-        pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
+        pxa.pxa_sparse_prefill_ex(cfg, budget, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
                                row_order=attn.row_order)
         evs[5].record(stream)
         torch.cuda.synchronize()
@@ -298,6 +301,29 @@ def main():
     torch.cuda.synchronize()
     dense_ms = e0.elapsed_time(e1) / a.dense_reps
     log(f"dense: {dense_ms:.3f} ms")
+
+    # the running-max skip is an approximation: its output against the same
+    # mask without the skip, and the dense kernel with the skip alone (context)
+    skip_cmp = None
+    if a.skip_threshold > 0:
+        o_ref = torch.empty_like(o)
+        pxa.pxa_sparse_prefill(cfg, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx,
+                               o_ref, row_order=attn.row_order)
+        pxa.pxa_sparse_prefill_ex(cfg, budget, dev["q"], dev["k"], dev["v"], attn.row_ptr,
+                                  attn.col_idx, o, row_order=attn.row_order)
+        torch.cuda.synchronize()
+        diff = (o.float() - o_ref.float()).abs()
+        e0.record(stream)
+        for _ in range(a.dense_reps):
+            pxa.pxa_dense_prefill_ex(cfg, budget, dev["q"], dev["k"], dev["v"], od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        skip_cmp = {"threshold": a.skip_threshold,
+                    "output_vs_no_skip_max_abs": round(float(diff.max()), 5),
+                    "output_vs_no_skip_mean_abs": round(float(diff.mean()), 7),
+                    "dense_with_skip_ms": round(e0.elapsed_time(e1) / a.dense_reps, 3)}
+        del o_ref, diff
+        log(f"running-max skip: {skip_cmp}")
 
     # context only: torch's own fused causal attention (flash backend) at the same shape,
     # to show the dense denominator is not a weak baseline
@@ -396,6 +422,7 @@ def main():
         "config": {"workload": f"{wl.name}: {wl.description}", "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": d, "seq_len": N, "block": B, "num_proxies": G, "gamma": gamma,
                    "batch": 1, "budget": budget_desc, "score_stride": a.score_stride,
+                   "skip_threshold": a.skip_threshold,
                    "input_sha256_16": digest},
         "speedup_vs_dense": round(dense_ms / ms_step, 3),
         "dense_ms": round(dense_ms, 3),
@@ -404,6 +431,7 @@ def main():
         "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
         "kept_density": round(density, 4),
         "mask_vs_every_query_scoring": stride_cmp,
+        "running_max_skip": skip_cmp,
         "k_h": kh.tolist() if kind != "ratio" else None,
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},
         "kept_block_mfma_util": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
