@@ -82,6 +82,8 @@ _SIGNATURES = {
     "pxa_validate_options": (ctypes.c_int, [_CFG, _OPT]),
     "pxa_proxy_score_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P]),
     "pxa_sparse_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "pxa_prefill_batch": (ctypes.c_int, [_CFG, _OPT, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                         _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_dense_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P]),
     "pxa_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
     "pxa_get_workspace_layout_ex": (ctypes.c_int, [_CFG, _OPT, ctypes.POINTER(pxa_workspace_layout)]),
@@ -379,3 +381,15 @@ def pxa_dense_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, strea
     _check(load_library().pxa_dense_prefill_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill_ex")
+
+
+def pxa_prefill_batch(cfg: Config, opts: Optional[Options], seq_lens, q, k, v, o, ws,
+                      ws_bytes=None, stream=None) -> None:
+    """seq_lens: host list of per-sequence token counts; q/k/v/o: the per-sequence
+    [heads][N_s][d] blocks stored one after another (flat bf16 tensors are fine)."""
+    n = len(seq_lens)
+    arr = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in seq_lens])
+    _check(load_library().pxa_prefill_batch(
+        ctypes.byref(cfg.c()), _bref(opts), n, arr if n else None, _tp(q, "bf16", "q"),
+        _tp(k, "bf16", "k"), _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"),
+        _nbytes(ws, ws_bytes), _stream(stream)), "pxa_prefill_batch")

@@ -348,4 +348,36 @@ int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void*
   return pxa_prefill_ex(cfg, nullptr, q, k, v, o, ws, ws_bytes, stream);
 }
 
+int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t num_seqs,
+                      const int32_t* seq_lens, const void* q, const void* k, const void* v,
+                      void* o, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_all(cfg, opts);
+  if (rc) return rc;
+  if (num_seqs < 1) return PXA_EINVAL;
+  if (!seq_lens) return PXA_ENULL;
+  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}, {ws, 256}}))) return rc;
+  if (ws_bytes < pxa_workspace_bytes_ex(cfg, opts)) return PXA_EWORKSPACE;
+  for (int32_t s = 0; s < num_seqs; ++s) {   // validate every length before any launch
+    const int32_t n = seq_lens[s];
+    if (n < 1 || n > cfg->seq_len) return PXA_EINVAL;
+    if (n % pxa::kBlockTokens) return PXA_EUNSUPPORTED;
+    pxa_config c = *cfg;
+    c.seq_len = n;
+    if ((rc = check_all(&c, opts))) return rc;   // e.g. a probe longer than this sequence
+  }
+  const size_t qrow = (size_t)cfg->num_heads * cfg->head_dim * 2;      // bytes per token
+  const size_t krow = (size_t)cfg->num_kv_heads * cfg->head_dim * 2;
+  size_t qoff = 0, koff = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    pxa_config c = *cfg;
+    c.seq_len = seq_lens[s];
+    rc = pxa_prefill_ex(&c, opts, (const char*)q + qoff, (const char*)k + koff,
+                        (const char*)v + koff, (char*)o + qoff, ws, ws_bytes, stream);
+    if (rc) return rc;
+    qoff += qrow * (size_t)c.seq_len;
+    koff += krow * (size_t)c.seq_len;
+  }
+  return PXA_OK;
+}
+
 }  // extern "C"

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 4
+#define PXA_ABI_VERSION 5
 
 enum {
   PXA_OK = 0,
@@ -156,6 +156,21 @@ int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void*
 int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q,
                    const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                    void* stream);
+
+/* Several sequences in one call (batched prefill, equal or different
+ * lengths).  Sequence s has seq_lens[s] tokens (host array; each a multiple of
+ * 128 and at most cfg->seq_len, which sizes the workspace); its tensors are
+ * the usual per-sequence blocks Q/O [H][N_s][d], K/V [Hkv][N_s][d], stored one
+ * after another (sequence s starts after the elements of sequences 0..s-1).
+ * The whole method runs on each sequence in order on `stream` with the same
+ * workspace (pxa_workspace_bytes_ex(cfg, opts)); the workspace keeps the
+ * intermediates of the last sequence.  Each sequence's output equals what
+ * pxa_prefill_ex gives for it alone.  PXA_EINVAL for num_seqs < 1 or a length
+ * above cfg->seq_len, PXA_EUNSUPPORTED for a length that is not a multiple of
+ * 128, PXA_ENULL for a NULL seq_lens. */
+int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t num_seqs,
+                      const int32_t* seq_lens, const void* q, const void* k, const void* v,
+                      void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 1, head pooling (blog post section 4, step 1 "Head Pooling"; section 3
  * calls it a simple pooling).  qbar[g] = mean of q over the group's query

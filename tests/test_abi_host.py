@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 4
+    assert pxa.pxa_abi_version() == 5
 
 
 def test_struct_layouts_match_header():
@@ -121,6 +121,25 @@ def test_attention_entry_points_validate_options_before_launch():
             A, A, A, A, stream=0)
     _expect(B.PXA_EALIGN, pxa.pxa_dense_prefill_ex, cfg, None, MIS, A, A, A, stream=0)
     _expect(B.PXA_ENULL, pxa.pxa_sparse_prefill_ex, cfg, None, A, A, A, None, A, A, stream=0)
+
+
+def test_batch_entry_point_validates_before_launch():
+    cfg = _good()                                   # seq_len 1024 sizes the workspace
+    big = pxa.pxa_workspace_bytes(cfg)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, None, [], A, A, A, A, A, ws_bytes=big, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, None, [256, 2048], A, A, A, A, A,
+            ws_bytes=big, stream=0)                 # longer than cfg.seq_len
+    _expect(B.PXA_EUNSUPPORTED, pxa.pxa_prefill_batch, cfg, None, [256, 200], A, A, A, A, A,
+            ws_bytes=big, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, pxa.Options.dynamic(4), [1024, 256],
+            A, A, A, A, A, ws_bytes=1 << 40, stream=0)   # probe of 4 blocks > 2 blocks
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_batch, cfg, None, [256], A, A, A, A, A,
+            ws_bytes=big - 256, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_prefill_batch, cfg, None, [256], MIS, A, A, A, A,
+            ws_bytes=big, stream=0)
+    lib = pxa.load_library()
+    assert lib.pxa_prefill_batch(ctypes.byref(cfg.c()), None, 1, None, A, A, A, A, A, big, None) \
+        == B.PXA_ENULL
 
 
 def test_budget_entry_points_validate_before_launch():
