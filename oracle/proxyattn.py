@@ -36,7 +36,11 @@ function that applies it):
   else nb;
 * selection: row I keeps the first min(k_h, I+1) blocks of its ranking plus
   the diagonal block I;
-* output: exact softmax renormalised over the kept causal keys.
+* output: exact softmax renormalised over the kept causal keys;
+* a sequence whose length N is not a multiple of B has nb = ceil(N / B)
+  blocks, the last one partial (N - (nb-1) B tokens): it takes part in every
+  step with the tokens it has (the probe of the budget is then the partial
+  block's queries; with a query stride its last query is always scored).
 
 parity: pinned (tests/test_oracle_pins.py, tests/test_golden.py).
 """
@@ -71,6 +75,17 @@ def group_query_heads(g: int, H: int, G: int) -> List[int]:
 def group_kv_heads(g: int, H: int, Hkv: int, G: int) -> List[int]:
     """Distinct KV heads used by the query heads of group g, ascending."""
     return sorted({kv_head_of(h, H, Hkv) for h in group_query_heads(g, H, G)})
+
+
+def num_blocks(N: int, block: int) -> int:
+    """Blocks of a sequence of N tokens: ceil(N / B).  When B does not divide N
+    the last block is partial and holds N - (nb-1) B tokens."""
+    return -(-N // block)
+
+
+def block_tokens(I: int, block: int, N: int) -> np.ndarray:
+    """Token indices of block I: [I B, min((I+1) B, N))."""
+    return np.arange(I * block, min((I + 1) * block, N))
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -125,20 +140,27 @@ def proxy_score_row(qbar_g: np.ndarray, kbar_g: np.ndarray, I: int, block: int,
 
     Blog post section 4, step 1 "Score Estimation": token-level proxy scores,
     then a block-level max pool (section 2 fixes the 128x128 block).  Causal
-    prefill: inside the diagonal block only keys j <= i count.
+    prefill: inside the diagonal block only keys j <= i count.  A partial last
+    block (B does not divide N) pools over the tokens it has.
 
     query_stride s > 1 is the sequence-level skip that section 5 credits for
     the low estimation cost, in this reading: only every s-th query of the
     block is scored, the queries at offsets s-1, 2s-1, ..., B-1 (the block's
-    last query, which sees the whole diagonal block, is always one of them);
-    every key is kept.  An approximation of the s = 1 score (never larger).
+    last query, which sees the whole diagonal block, is always one of them; in
+    a partial block its last query is added when the offsets miss it); every
+    key is kept.  An approximation of the s = 1 score (never larger).
     """
     if query_stride < 1 or block % query_stride:
         raise ValueError("query_stride must divide the block")
-    rows = np.arange(I * block + query_stride - 1, (I + 1) * block, query_stride)
-    L = scale * (qbar_g[rows] @ kbar_g[: (I + 1) * block].T)      # [B/s, (I+1)B]
-    j_idx = np.arange((I + 1) * block)[None, :]
-    L = np.where(j_idx <= rows[:, None], L, NEG_INF)
+    N = qbar_g.shape[0]
+    toks = block_tokens(I, block, N)
+    rows = toks[query_stride - 1::query_stride]
+    if toks.size % query_stride:                  # partial block: its last query too
+        rows = np.append(rows, toks[-1])
+    nkeys = min((I + 1) * block, N)
+    L = scale * (qbar_g[rows] @ kbar_g[:nkeys].T)                 # [queries, keys]
+    L = np.where(np.arange(nkeys)[None, :] <= rows[:, None], L, NEG_INF)
+    L = np.pad(L, ((0, 0), (0, (I + 1) * block - nkeys)), constant_values=NEG_INF)
     return L.reshape(rows.size, I + 1, block).max(axis=(0, 2))
 
 
@@ -152,7 +174,7 @@ def proxy_scores(qbar: np.ndarray, kbar: np.ndarray, block: int = 128,
     """
     G, N, d = qbar.shape
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    nb = N // block
+    nb = num_blocks(N, block)
     S = np.full((G, nb, nb), NEG_INF)
     for g in range(G):
         for I in (range(nb) if rows is None else rows):
@@ -183,21 +205,14 @@ def last_block_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int,
     """Mean causal attention mass per key block for the last query block.
 
     Blog post section 4, step 2: the last small portion of query blocks is
-    used to estimate each head's block-level sparsity.  Reading: the last full
-    block of B queries; each query's exact softmax over its causal keys; the
-    per-block mass is averaged over the B queries (so the masses sum to 1).
+    used to estimate each head's block-level sparsity.  Reading: the last
+    query block (B queries, or the tokens of a partial last block); each
+    query's exact softmax over its causal keys; the per-block mass is averaged
+    over those queries (so the masses sum to 1).
 
     q_h: [N, d] one query head, k_kv: [N, d] its KV head -> m: [nb] float64.
     """
-    N = q_h.shape[0]
-    nb = N // block
-    T = np.arange(N - block, N)
-    L = scale * (np.asarray(q_h[T], dtype=np.float64) @ np.asarray(k_kv, dtype=np.float64).T)
-    L = np.where(np.arange(N)[None, :] <= T[:, None], L, NEG_INF)
-    L = L - L.max(axis=1, keepdims=True)
-    P = np.exp(L)
-    P /= P.sum(axis=1, keepdims=True)
-    return P.reshape(block, nb, block).sum(axis=2).mean(axis=0)
+    return last_blocks_masses(q_h, k_kv, block, scale, 1)
 
 
 def last_blocks_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int, scale: float,
@@ -205,29 +220,33 @@ def last_blocks_masses(q_h: np.ndarray, k_kv: np.ndarray, block: int, scale: flo
     """Mean causal attention mass per key block over the last m query blocks.
 
     Blog post section 4, step 2 probes "the last small portion" of the query
-    blocks.  Reading for a probe of m >= 1 blocks: the probe set is the last
-    m * B queries; each query's exact softmax over its causal keys; the mass a
+    blocks.  Reading for a probe of m >= 1 blocks: the probe set is every
+    query of the last m blocks (m B queries, fewer when the last block is
+    partial); each query's exact softmax over its causal keys; the mass a
     query puts in key block J is summed over J's keys, then averaged over the
-    whole probe set (so the masses sum to 1).  m = 1 gives last_block_masses.
+    whole probe set (so the masses sum to 1).
 
     q_h: [N, d] one query head, k_kv: [N, d] its KV head -> [nb] float64.
     """
     N = q_h.shape[0]
-    nb = N // block
+    nb = num_blocks(N, block)
     if not 1 <= m <= nb:
         raise ValueError("m must lie in [1, nb]")
     q64 = np.asarray(q_h, dtype=np.float64)
     k64 = np.asarray(k_kv, dtype=np.float64)
     total = np.zeros(nb)
+    count = 0
     for I in range(nb - m, nb):                  # one probe query block at a time
-        rows = np.arange(I * block, (I + 1) * block)
+        rows = block_tokens(I, block, N)
         L = scale * (q64[rows] @ k64.T)
         L = np.where(np.arange(N)[None, :] <= rows[:, None], L, NEG_INF)
         L = L - L.max(axis=1, keepdims=True)
         P = np.exp(L)
         P /= P.sum(axis=1, keepdims=True)
-        total += P.reshape(block, nb, block).sum(axis=2).sum(axis=0)
-    return total / (m * block)
+        P = np.pad(P, ((0, 0), (0, nb * block - N)))           # empty tail of a partial block
+        total += P.reshape(rows.size, nb, block).sum(axis=2).sum(axis=0)
+        count += rows.size
+    return total / count
 
 
 def ratio_count(I: int, ratio: float) -> int:
@@ -270,7 +289,7 @@ def budgets(q: np.ndarray, k: np.ndarray, S: np.ndarray, G: int, gamma: float,
     H, N, d = q.shape
     Hkv = k.shape[0]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    nb = N // block
+    nb = num_blocks(N, block)
     kh = np.zeros(H, dtype=np.int64)
     masses = np.zeros((H, nb))
     for h in range(H):
@@ -332,13 +351,15 @@ def sparse_attention_row(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
 
     Standard attention (blog post section 2: softmax-normalised q.k weights
     applied to v), restricted to the keys of the kept blocks and to j <= i,
-    renormalised over those keys.  Returns [B, d] float64.
+    renormalised over those keys.  Returns [B, d] float64 ([r, d] for a
+    partial last block of r tokens).
     """
-    qi = np.asarray(q_h[I * block:(I + 1) * block], dtype=np.float64)
-    cols = np.concatenate([np.arange(J * block, (J + 1) * block) for J in blocks])
+    N = q_h.shape[0]
+    qrows = block_tokens(I, block, N)
+    qi = np.asarray(q_h[qrows], dtype=np.float64)
+    cols = np.concatenate([block_tokens(J, block, N) for J in blocks])
     L = scale * (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)
-    i_idx = np.arange(I * block, (I + 1) * block)[:, None]
-    L = np.where(cols[None, :] <= i_idx, L, NEG_INF)
+    L = np.where(cols[None, :] <= qrows[:, None], L, NEG_INF)
     L = L - L.max(axis=1, keepdims=True)
     P = np.exp(L)
     P /= P.sum(axis=1, keepdims=True)
@@ -361,25 +382,30 @@ def sparse_attention_row_skip(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarra
     for `group` consecutive queries together (all of them must satisfy it);
     a skipped block leaves the running state untouched.
 
-    Returns (out [B, d] float64, skipped: list of (block J, group index)).
+    A partial last block (r < B queries) has ceil(r / group) groups, the last
+    one short; keys past the sequence end do not exist.
+
+    Returns (out [B or r, d] float64, skipped: list of (block J, group index)).
     """
-    q64 = np.asarray(q_h[I * block:(I + 1) * block], dtype=np.float64)
+    N = q_h.shape[0]
+    qi = block_tokens(I, block, N)
+    nq = qi.size
+    q64 = np.asarray(q_h[qi], dtype=np.float64)
     k64 = np.asarray(k_kv, dtype=np.float64)
     v64 = np.asarray(v_kv, dtype=np.float64)
     d = v64.shape[1]
-    qi = np.arange(I * block, (I + 1) * block)
-    m = np.full(block, NEG_INF)
-    lsum = np.zeros(block)
-    acc = np.zeros((block, d))
+    m = np.full(nq, NEG_INF)
+    lsum = np.zeros(nq)
+    acc = np.zeros((nq, d))
     skipped = []
     log_thr = math.log(threshold)
     for J in sorted((int(b) for b in blocks if 0 <= b <= I), reverse=True):
-        cols = np.arange(J * block, (J + 1) * block)
+        cols = block_tokens(J, block, N)
         L = scale * (q64 @ k64[cols].T)
         L = np.where(cols[None, :] <= qi[:, None], L, NEG_INF)
         tmax = L.max(axis=1)
-        for gi in range(block // group):
-            rows = slice(gi * group, (gi + 1) * group)
+        for gi in range(-(-nq // group)):
+            rows = slice(gi * group, min((gi + 1) * group, nq))
             mg, tg = m[rows], tmax[rows]
             if np.all(np.isfinite(mg)) and np.all(tg - mg < log_thr):
                 skipped.append((J, gi))
@@ -402,7 +428,7 @@ def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarr
     H, N, d = q.shape
     Hkv = k.shape[0]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    nb = N // block
+    nb = num_blocks(N, block)
     out = np.zeros((H, N, d))
     for h in (range(H) if heads is None else heads):
         kv = kv_head_of(h, H, Hkv)

@@ -26,7 +26,7 @@ def _brute_logit(qv, kv, scale):
 def _brute_block_scores(qp, kp, block, scale):
     """Loops over every causal token pair and keeps the max per block pair."""
     N = qp.shape[0]
-    nb = N // block
+    nb = -(-N // block)                      # a partial last block counts
     S = [[-math.inf] * nb for _ in range(nb)]
     for i in range(N):
         for j in range(i + 1):
@@ -516,3 +516,132 @@ def test_skip_set_grows_with_threshold_and_error_is_bounded():
         # a skipped block holds at most 16 keys of weight < lam * max weight each
         assert np.max(np.abs(out - exact)) <= 2 * 16 * len(blocks) * lam * np.abs(v).max() + 1e-12
     assert prev                                             # something was skipped at 0.1
+
+
+# ---------------------------------------------------------------- partial last block (B does not divide N)
+@pytest.mark.parametrize("block,N,d", [(4, 14, 3), (8, 21, 4), (8, 5, 3), (4, 13, 2)])
+def test_ragged_scores_equal_bruteforce_maxpool(block, N, d):
+    qp, kp = _rand((2, N, d), 90), _rand((2, N, d), 91)
+    S = O.proxy_scores(qp, kp, block, 0.45)
+    assert S.shape == (2, -(-N // block), -(-N // block))
+    for g in range(2):
+        np.testing.assert_allclose(S[g], _brute_block_scores(qp[g], kp[g], block, 0.45), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("s,N", [(2, 29), (4, 29), (4, 30), (2, 25), (4, 3)])
+def test_ragged_strided_scores_bruteforce(s, N):
+    # scored: offsets s-1, 2s-1, ... of each block, and the sequence's last query
+    B, d, scale = 8, 3, 0.5
+    qp, kp = _rand((N, d), 92), _rand((N, d), 93)
+    nb = -(-N // B)
+    want = [[-math.inf] * nb for _ in range(nb)]
+    for i in range(N):
+        if (i % B) % s != s - 1 and i != N - 1:
+            continue
+        for j in range(i + 1):
+            x = _brute_logit(qp[i], kp[j], scale)
+            want[i // B][j // B] = max(want[i // B][j // B], x)
+    got = O.proxy_scores(qp[None], kp[None], B, scale, query_stride=s)[0]
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-12)
+
+
+def _brute_ragged_probe_masses(q, k, block, scale, m):
+    """Pure-Python loops over every query of the last m blocks, the last partial."""
+    N = q.shape[0]
+    nb = -(-N // block)
+    probe = range((nb - m) * block, N)
+    out = [0.0] * nb
+    for i in probe:
+        w = [math.exp(_brute_logit(q[i], k[j], scale)) for j in range(i + 1)]
+        z = math.fsum(w)
+        for j, wj in enumerate(w):
+            out[j // block] += wj / z / len(probe)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("N,m", [(27, 1), (27, 2), (27, 4), (9, 1), (17, 3)])
+def test_ragged_probe_masses_bruteforce_and_sum_to_one(N, m):
+    q, k = _rand((N, 3), 94, 1.8), _rand((N, 3), 95)
+    got = O.last_blocks_masses(q, k, 8, 0.6, m)
+    np.testing.assert_allclose(got, _brute_ragged_probe_masses(q, k, 8, 0.6, m), rtol=1e-12, atol=1e-15)
+    assert got.sum() == pytest.approx(1.0, abs=1e-12)
+    if m == 1:
+        np.testing.assert_allclose(O.last_block_masses(q, k, 8, 0.6), got, rtol=1e-14, atol=1e-16)
+
+
+def test_ragged_probe_masses_uniform_logits_closed_form():
+    # q = 0: query i spreads 1/(i+1) over keys 0..i; the probe is the 5 queries
+    # of the partial last block (N = 21, B = 8 -> blocks of 8, 8, 5).
+    N, B = 21, 8
+    q, k = np.zeros((N, 2)), _rand((N, 2), 96)
+    want = np.zeros(3)
+    for i in range(16, 21):
+        for J in range(3):
+            cnt = max(0, min(i, (J + 1) * B - 1) - J * B + 1)
+            want[J] += cnt / (i + 1) / 5
+    np.testing.assert_allclose(O.last_block_masses(q, k, B, 1.0), want, rtol=1e-13, atol=1e-16)
+
+
+def test_ragged_dense_attention_equals_library_causal_attention():
+    H, Hkv, N, d, B = 4, 2, 27, 8, 8
+    q, k, v = _rand((H, N, d), 97, 1.5), _rand((Hkv, N, d), 98), _rand((Hkv, N, d), 99)
+    out = O.sparse_attention(q, k, v, O.causal_keep(H, 4), B, 0.4)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.4, causal=True), rtol=1e-12, atol=1e-12)
+
+
+def test_ragged_any_mask_equals_dense_with_minus_inf_bias():
+    H, Hkv, N, d, B = 2, 1, 22, 4, 4
+    nb = 6
+    rng = np.random.default_rng(100)
+    q, k, v = _rand((H, N, d), 101), _rand((Hkv, N, d), 102), _rand((Hkv, N, d), 103)
+    keep = np.tril(rng.random((H, nb, nb)) < 0.5)
+    for I in range(nb):
+        keep[:, I, I] = True
+    tok = np.repeat(np.repeat(keep, B, axis=1), B, axis=2)[:, :N, :N] & np.tril(np.ones((N, N), dtype=bool))
+    out = O.sparse_attention(q, k, v, keep, B, 0.5)
+    np.testing.assert_allclose(out, _sdpa64(q, k, v, 0.5, mask=tok), rtol=1e-12, atol=1e-12)
+
+
+def test_ragged_pipeline_gamma_one_is_dense_and_prefix_rows_are_causal():
+    H, Hkv, N, d, B, G = 4, 2, 30, 4, 8, 2
+    q, k, v = _rand((H, N, d), 104, 0.5), _rand((Hkv, N, d), 105), _rand((Hkv, N, d), 106)
+    r = O.pipeline(q, k, v, G, 1.0, block=B)
+    assert r["keep"].sum() == H * 4 * 5 // 2
+    np.testing.assert_allclose(r["o"], _sdpa64(q, k, v, 1 / math.sqrt(d), causal=True), rtol=1e-12, atol=1e-12)
+    # causality: rows before the partial block score as in the truncated sequence
+    t = O.pipeline(q[:, :24].copy(), k[:, :24].copy(), v[:, :24].copy(), G, 0.9, block=B, with_output=False)
+    np.testing.assert_array_equal(r["S"][:, :3, :3], t["S"])
+
+
+def test_ragged_skip_bruteforce_short_last_group():
+    # partial query block of 10 rows, groups of 4 -> groups of 4, 4 and 2 rows
+    N, d, B, Gq = 42, 3, 16, 4
+    q, k, v = _rand((N, d), 107), _rand((N, d), 108), _rand((N, d), 109)
+    q[:, 0] += 2.0
+    k[32:, 0] += 2.0              # the diagonal keys dominate, so earlier blocks can be skipped
+    I, blocks, lam, scale = 2, [0, 1, 2], 0.5, 1.0
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam, group=Gq)
+    nq = N - I * B
+    m, l = [-math.inf] * nq, [0.0] * nq
+    acc = [[0.0] * d for _ in range(nq)]
+    want_skip = []
+    for J in (2, 1, 0):
+        keys = range(J * B, min((J + 1) * B, N))
+        logits = [[(scale * sum(q[I * B + i][c] * k[j][c] for c in range(d)) if j <= I * B + i else -math.inf)
+                   for j in keys] for i in range(nq)]
+        for gi in range(3):
+            rows = range(gi * Gq, min((gi + 1) * Gq, nq))
+            if all(m[i] > -math.inf and math.exp(max(logits[i]) - m[i]) < lam for i in rows):
+                want_skip.append((J, gi))
+                continue
+            for i in rows:
+                mn = max(m[i], max(logits[i]))
+                a = math.exp(m[i] - mn) if m[i] > -math.inf else 0.0
+                w = [math.exp(x - mn) if x > -math.inf else 0.0 for x in logits[i]]
+                l[i] = l[i] * a + math.fsum(w)
+                for c in range(d):
+                    acc[i][c] = acc[i][c] * a + math.fsum(wj * v[j][c] for wj, j in zip(w, keys))
+                m[i] = mn
+    assert skipped == want_skip and (1, 2) in want_skip      # the short group is skipped too
+    assert out.shape == (nq, d)
+    np.testing.assert_allclose(out, np.array(acc) / np.array(l)[:, None], rtol=1e-12, atol=1e-14)
