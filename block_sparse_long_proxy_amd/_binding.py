@@ -131,7 +131,8 @@ class Config:
 
     @property
     def nb(self) -> int:
-        return self.seq_len // self.block
+        """Blocks: ceil(N / B); the last one is partial when B does not divide N."""
+        return -(-self.seq_len // self.block)
 
     @property
     def scale(self) -> float:

@@ -246,13 +246,13 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
 }
 
 size_t select_ws_bytes(const LaunchArgs& a) {   // row lengths + the longest-first order
-  return 2 * align_up((size_t)a.H * (a.N / kBlock) * sizeof(int32_t), 256);
+  return 2 * align_up((size_t)a.H * num_blocks(a.N) * sizeof(int32_t), 256);
 }
 
 hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
                          int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
                          hipStream_t stream) {
-  const int nb = a.N / kBlock;
+  const int nb = num_blocks(a.N);
   int32_t* counts = (int32_t*)ws;
   int32_t* tmp = (int32_t*)((char*)ws + align_up((size_t)a.H * nb * sizeof(int32_t), 256));
   hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,

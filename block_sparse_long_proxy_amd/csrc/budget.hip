@@ -3,7 +3,8 @@
 // ProxyAttn blog post (ir.hit.edu.cn), section 4, step 2: the last small part
 // of the query blocks estimates each head's block-level sparsity, so heads
 // that share one importance ranking get different block budgets.  Reading:
-// the probe is the last m full query blocks (m = 1 by default: 128 queries);
+// the probe is every query of the last m query blocks (m = 1 by default: 128
+// queries, fewer when the last block is partial);
 // each probe query's exact causal softmax; masses[h][J] = mean over the probe
 // queries of the probability mass in key block J; k_h = fewest leading blocks
 // of the group's ranking of row nb-1 (score descending, block ascending on
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, float* __restrict__ lse,
     int H, int Hkv, int N, int m, float scale_log2) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
-  const int nb = N / kBlock;
+  const int nb = (N + kBlock - 1) / kBlock;
   const int h = blockIdx.y;
   const int z = blockIdx.z;                // probe block z of m
   const int kvh = h / (H / Hkv);
@@ -44,13 +45,14 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
   const int j1 = min(I + 1, j0 + kLseBlocksPerWG);   // causal key blocks only
   if (j0 >= j1) return;
   bf16x8 qf[D / 16];
-  load_qfrag<D>(q + ((size_t)h * N + (size_t)I * kBlock + qloc) * D, qf);
+  // rows past a partial last block repeat token N-1 (excluded from the masses)
+  load_qfrag<D>(q + ((size_t)h * N + (size_t)min(I * kBlock + qloc, N - 1)) * D, qf);
   const __bf16* kb = k + (size_t)kvh * N * D;
   float* out = lse + ((size_t)h * m + z) * nb * kBlock;
 
   for (int J = j0; J < j1; ++J) {
     __syncthreads();
-    stage_ktile<D>(kb + (size_t)J * kBlock * D, ks);
+    stage_ktile<D>(kb + (size_t)J * kBlock * D, ks, min(kBlock, N - J * kBlock));
     __syncthreads();
     f32x16 s[4];
     tile_scores<D>(ks, qf, s);
@@ -99,7 +101,7 @@ __device__ __forceinline__ void bitonic_sort_u64(uint64_t* keys, int P) {
 
 __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
     const float* __restrict__ lse, const float* __restrict__ scores, int32_t* __restrict__ k_h,
-    float* __restrict__ masses, int H, int G, int nb, int m, int P, float gamma) {
+    float* __restrict__ masses, int H, int G, int nb, int m, int P, float gamma, int tail) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);              // [P]
   float* mass = reinterpret_cast<float*>(keys + P);                 // [nb]
@@ -151,12 +153,15 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
       qlse[t] = mx + log2f(sm);
     }
     __syncthreads();
-    // 2. block masses: one wave per block J, lanes over the 128 queries.
+    // 2. block masses: one wave per block J, lanes over the 128 queries (only
+    //    the `rows` that exist in a partial last block).
     {
       const int wv = t >> 6, ln = t & 63, nw = kFinThreads / 64;
+      const int rows = I == nb - 1 ? tail : kBlock;
       for (int J = wv; J <= I; J += nw) {
         const float* r = L + (size_t)J * kBlock;
-        float v = exp2f(r[ln] - qlse[ln]) + exp2f(r[ln + 64] - qlse[ln + 64]);
+        float v = (ln < rows ? exp2f(r[ln] - qlse[ln]) : 0.f) +
+                  (ln + 64 < rows ? exp2f(r[ln + 64] - qlse[ln + 64]) : 0.f);
         v = wave_sum(v);
         if (ln == 0) mass[J] += v;
       }
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
     __syncthreads();   // qlse / part arrays are reused by the next probe block
   }
   {
-    const float inv = 1.0f / (float)(m * kBlock);
+    const float inv = 1.0f / (float)((m - 1) * kBlock + tail);   // probe queries
     for (int J = t; J < nb; J += kFinThreads) {
       mass[J] *= inv;
       masses[(size_t)h * nb + J] = mass[J];
@@ -209,7 +214,7 @@ static int pow2_at_least(int n) {
 
 size_t budget_ws_bytes(const LaunchArgs& a) {   // lse [H][m][nb][128]
   const size_t m = a.budget_mode == kBudgetDynamic ? (size_t)a.last_blocks : 1;
-  return align_up((size_t)a.H * m * (a.N / kBlock) * kBlock * sizeof(float), 256);
+  return align_up((size_t)a.H * m * num_blocks(a.N) * kBlock * sizeof(float), 256);
 }
 
 __global__ void budget_fixed_kernel(int32_t* __restrict__ k_h, int H, int k) {
@@ -225,7 +230,8 @@ hipError_t launch_fixed_budget(const LaunchArgs& a, int32_t* k_h, hipStream_t st
 
 hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, const float* scores,
                          int32_t* k_h, float* masses, void* ws, hipStream_t stream) {
-  const int nb = a.N / kBlock;
+  const int nb = num_blocks(a.N);
+  const int tail = a.N - (nb - 1) * kBlock;
   float* lse = (float*)ws;
   const float sl2 = a.scale * kLog2e;
   const int m = a.last_blocks;
@@ -241,7 +247,7 @@ hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, cons
   const int P = pow2_at_least(nb);
   const size_t smem = (size_t)P * 8 + (size_t)nb * 4 + (size_t)kBlock * 4 * 9 + kFinThreads * 4;
   hipLaunchKernelGGL(budget_finalize_kernel, dim3(a.H), dim3(kFinThreads), smem, stream, lse,
-                     scores, k_h, masses, a.H, a.G, nb, m, P, a.gamma);
+                     scores, k_h, masses, a.H, a.G, nb, m, P, a.gamma, tail);
   return hipGetLastError();
 }
 

@@ -75,7 +75,8 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], float mx, bf16x8 
 }
 
 // One pipeline step on key block J (tiles already in LDS / landing): S, the
-// softmax, then O += V P, issuing the copies of block Jn (< 0: none).
+// softmax, then O += V P, issuing the copies of block Jn (knext / vnext NULL:
+// none; next_rows < 128: Jn is a partial last block).
 // skip_delta (raw logit units, -inf: off): the running-max skip of the
 // BLASST pages -- when every query of the wave has its tile max below
 // m_run + skip_delta, the wave drops the tile's softmax and PV product.
@@ -84,7 +85,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
                                         __bf16* vs, const bf16x8 (&qf)[D / 16],
                                         f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
                                         float scale_log2, int qloc, const __bf16* knext,
-                                        const __bf16* vnext, float skip_delta) {
+                                        const __bf16* vnext, int next_rows, float skip_delta) {
   f32x16 s[4];
   // S^T = K Q^T with the four K fragments of k-step ss+1 read while the four
   // products of step ss issue (scheduling barriers keep that order).
@@ -122,7 +123,10 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
 
   wait_vmem();                   // this thread's part of V(J) has landed
   __syncthreads();               // V(J) visible; every wave is done with the K tile
-  if (knext) tile_load_lds<D, false>(knext, ks);
+  if (knext) {
+    if (next_rows < kBlock) tile_load_lds_rows<D, false>(knext, ks, next_rows);
+    else tile_load_lds<D, false>(knext, ks);
+  }
 
   if (!skip) {
 #pragma unroll
@@ -136,7 +140,10 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
 
   wait_vmem();                   // this thread's part of K(Jn) has landed
   __syncthreads();               // K(Jn) visible; every wave is done with the V tile
-  if (vnext) tile_load_lds<D, true>(vnext, vs);
+  if (vnext) {
+    if (next_rows < kBlock) tile_load_lds_rows<D, true>(vnext, vs, next_rows);
+    else tile_load_lds<D, true>(vnext, vs);
+  }
 }
 
 template <int D, bool DENSE>
@@ -148,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];   // K tile, kswz layout
   __shared__ __attribute__((aligned(16))) __bf16 vs[kBlock * D];   // V tile, vswz layout
 
-  const int nb = N / kBlock;
+  const int nb = (N + kBlock - 1) / kBlock;
   int h, I;
   if (!DENSE && row_order) {
     const int r = row_order[blockIdx.x];
@@ -183,8 +190,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   const __bf16* vbase = v + (size_t)kvh * N * D;
   constexpr size_t kTile = (size_t)kBlock * D;
 
+  // Queries past the end of a partial last block read token N-1 (their
+  // outputs are never stored); that block's missing keys read token N-1 too
+  // and are masked by causality for every query that exists.
+  const int qtok = I * kBlock + qloc;
   bf16x8 qf[D / 16];
-  load_qfrag<D>(q + ((size_t)h * N + (size_t)I * kBlock + qloc) * D, qf);
+  load_qfrag<D>(q + ((size_t)h * N + (size_t)min(qtok, N - 1)) * D, qf);
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -215,11 +226,21 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     return -1;
   };
 
+  // Tokens of key block J (fewer than 128 only in a partial last block, which
+  // with ascending columns can only be this first tile; checked everywhere so
+  // that no column list makes a copy read past the end of K or V).
+  auto rows_of = [&](int J) { return min(kBlock, N - J * kBlock); };
   int it = end - 1;
   int J = next_block(it);
   if (J >= 0) {
-    tile_load_lds<D, false>(kbase + (size_t)J * kTile, ks);
-    tile_load_lds<D, true>(vbase + (size_t)J * kTile, vs);
+    const int rows = rows_of(J);
+    if (rows < kBlock) {
+      tile_load_lds_rows<D, false>(kbase + (size_t)J * kTile, ks, rows);
+      tile_load_lds_rows<D, true>(vbase + (size_t)J * kTile, vs, rows);
+    } else {
+      tile_load_lds<D, false>(kbase + (size_t)J * kTile, ks);
+      tile_load_lds<D, true>(vbase + (size_t)J * kTile, vs);
+    }
   }
   wait_vmem();
   __syncthreads();
@@ -229,7 +250,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int Jn = next_block(it);
     fa_step<D, true>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                      Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
-                     Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr, skip_delta);
+                     Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr,
+                     Jn >= 0 ? rows_of(Jn) : kBlock, skip_delta);
     J = Jn;
   }
   while (J >= 0) {
@@ -237,13 +259,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const int Jn = next_block(it);
     fa_step<D, false>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                       Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
-                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr, skip_delta);
+                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr,
+                      Jn >= 0 ? rows_of(Jn) : kBlock, skip_delta);
     J = Jn;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-  __bf16* orow = o + ((size_t)h * N + (size_t)I * kBlock + qloc) * D;
+  if (qtok >= N) return;          // no barrier follows
+  __bf16* orow = o + ((size_t)h * N + (size_t)qtok) * D;
   const int hi = l >> 5;
 #pragma unroll
   for (int m = 0; m < D / 32; ++m) {
@@ -261,7 +285,7 @@ template <int D>
 static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, const void* v,
                             const int32_t* row_ptr, const int32_t* col_idx,
                             const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
-  const dim3 grid(a.H * (a.N / kBlock)), block(kThreads);
+  const dim3 grid(a.H * num_blocks(a.N)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   // skip when scale * (tile max - running max) < ln(threshold)
   const float skip_delta = a.skip_threshold > 0.f ? std::log(a.skip_threshold) / a.scale : -INFINITY;

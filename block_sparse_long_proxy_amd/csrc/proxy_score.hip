@@ -6,6 +6,10 @@
 // Causal prefill: in the diagonal block only keys j <= i count; blocks above
 // the diagonal get -inf.
 //
+// A partial last block (128 does not divide N) is read with its missing rows
+// replaced by copies of token N-1: every pair such a copy forms is a causal
+// pair of token N-1, so its block maxima are those of the tokens present.
+//
 // With a query stride s (the sequence-level skip of section 5, read as
 // scoring every s-th query of a block: offsets s-1, 2s-1, ..., 127) a
 // workgroup serves s consecutive rows, 128/s queries each, so the per-tile
@@ -44,7 +48,8 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
   __shared__ float wm[2][R][kWaves][64];         // per-wave maxima of one 64-tile chunk
 
-  const int nb = N / kBlock;
+  const int nb = (N + kBlock - 1) / kBlock;
+  const int tail = N - (nb - 1) * kBlock;        // tokens of the last block (128 unless partial)
   const int g = (int)(blockIdx.x % G);
   const int I0 = nb - 1 - R * (int)(blockIdx.x / G);   // top row; longest rows first
   const int ws = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // keys 32 ws ..
@@ -59,7 +64,11 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   for (int c = 0; c < 4; ++c) {
     const int Ir = I0 - c / QC;
     if (Ir >= 0) {
-      load_qfrag<D>(qbar + ((size_t)g * N + (size_t)Ir * kBlock + qoff(c)) * D, qf[c]);
+      // past the end of a partial last block: a copy of token N-1, whose pairs
+      // with the (equally clamped) keys are all causal pairs of token N-1, so
+      // the block maxima are unchanged
+      const int qt = min(Ir * kBlock + qoff(c), N - 1);
+      load_qfrag<D>(qbar + ((size_t)g * N + (size_t)qt) * D, qf[c]);
     } else {
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) qf[c][s] = bf16x8{};
@@ -88,14 +97,21 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     }
   };
 
-  tile_load_lds<D, false>(kb, kt[0]);
+  // key tile J into buffer b; only tile nb-1 can be partial
+  auto load_tile = [&](int J, __bf16* buf) {
+    if (J == nb - 1 && tail < kBlock)
+      tile_load_lds_rows<D, false>(kb + (size_t)J * kTile, buf, tail);
+    else
+      tile_load_lds<D, false>(kb + (size_t)J * kTile, buf);
+  };
+  load_tile(0, kt[0]);
   float keep[R];                                 // this wave's max of tile J per row, lane J mod 64
 #pragma unroll
   for (int r = 0; r < R; ++r) keep[r] = -INFINITY;
   for (int J = 0; J <= I0; ++J) {
     wait_vmem();       // this thread's part of tile J (the only copy in flight)
     __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
-    if (J + 1 <= I0) tile_load_lds<D, false>(kb + (size_t)(J + 1) * kTile, kt[(J + 1) % kScoreBufs]);
+    if (J + 1 <= I0) load_tile(J + 1, kt[(J + 1) % kScoreBufs]);
     if (J > 0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
     const __bf16* cur = kt[J % kScoreBufs];
     f32x16 acc[4];
@@ -150,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,
                               float* scores, hipStream_t stream) {
-  const int nb = a.N / kBlock;
+  const int nb = num_blocks(a.N);
   const dim3 grid(a.G * ((nb + a.score_stride - 1) / a.score_stride)), block(kThreads);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)qbar, (const __bf16*)kbar,

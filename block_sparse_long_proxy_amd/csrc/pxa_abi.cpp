@@ -33,8 +33,8 @@ int check_config(const pxa_config* c) {
   if (std::isnan(c->softmax_scale) || std::isinf(c->softmax_scale)) return PXA_EINVAL;
   if (c->block != pxa::kBlockTokens) return PXA_EUNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return PXA_EUNSUPPORTED;
-  if (c->seq_len % pxa::kBlockTokens || c->seq_len > kMaxSeq) return PXA_EUNSUPPORTED;
-  const int64_t nb = c->seq_len / pxa::kBlockTokens;
+  if (c->seq_len > kMaxSeq) return PXA_EUNSUPPORTED;
+  const int64_t nb = pxa::num_blocks(c->seq_len);   // the last block may be partial
   if ((int64_t)c->num_heads * nb * (nb + 1) / 2 > INT32_MAX) return PXA_EUNSUPPORTED;
   return PXA_OK;
 }
@@ -42,7 +42,7 @@ int check_config(const pxa_config* c) {
 // Method-variant check against a valid configuration; NULL is the default.
 int check_budget(const pxa_config* c, const pxa_options* b) {
   if (!b) return PXA_OK;
-  const int nb = c->seq_len / pxa::kBlockTokens;
+  const int nb = pxa::num_blocks(c->seq_len);
   if (b->score_stride != 1 && b->score_stride != 2 && b->score_stride != 4) return PXA_EINVAL;
   if (!std::isfinite(b->skip_threshold) || b->skip_threshold < 0.f || b->skip_threshold > 1.f)
     return PXA_EINVAL;
@@ -113,7 +113,7 @@ int hip_rc(hipError_t e) {
 
 void layout_of(const pxa_config* c, const pxa_options* b, pxa_workspace_layout* L) {
   const pxa::LaunchArgs a = args_of(c, b);
-  const size_t nb = (size_t)a.N / pxa::kBlockTokens;
+  const size_t nb = (size_t)pxa::num_blocks(a.N);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -143,7 +143,7 @@ const char* pxa_strerror(int code) {
   switch (code) {
     case PXA_OK: return "ok";
     case PXA_EINVAL: return "invalid configuration (shape, grouping, gamma, scale or budget)";
-    case PXA_EUNSUPPORTED: return "unsupported configuration (head_dim, block, seq_len)";
+    case PXA_EUNSUPPORTED: return "unsupported configuration (head_dim, block, seq_len too large)";
     case PXA_ENULL: return "null pointer";
     case PXA_EALIGN: return "misaligned pointer";
     case PXA_EWORKSPACE: return "workspace too small";
@@ -183,7 +183,7 @@ size_t pxa_select_workspace_bytes(const pxa_config* cfg) {
 
 size_t pxa_max_col_entries(const pxa_config* cfg) {
   if (check_config(cfg) != PXA_OK) return 0;
-  const size_t nb = (size_t)cfg->seq_len / pxa::kBlockTokens;
+  const size_t nb = (size_t)pxa::num_blocks(cfg->seq_len);
   return (size_t)cfg->num_heads * nb * (nb + 1) / 2;
 }
 
@@ -360,7 +360,6 @@ int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t nu
   for (int32_t s = 0; s < num_seqs; ++s) {   // validate every length before any launch
     const int32_t n = seq_lens[s];
     if (n < 1 || n > cfg->seq_len) return PXA_EINVAL;
-    if (n % pxa::kBlockTokens) return PXA_EUNSUPPORTED;
     pxa_config c = *cfg;
     c.seq_len = n;
     if ((rc = check_all(&c, opts))) return rc;   // e.g. a probe longer than this sequence

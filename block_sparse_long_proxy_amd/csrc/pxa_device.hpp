@@ -58,13 +58,16 @@ struct KStage {
   u32x4 r[kChunks];
 };
 
+// rows < 128: a partial tile; rows past the end repeat row rows-1.
 template <int D>
-__device__ __forceinline__ void kstage_load(const __bf16* __restrict__ g, KStage<D>& st) {
+__device__ __forceinline__ void kstage_load(const __bf16* __restrict__ g, KStage<D>& st,
+                                            int rows = kBlock) {
   constexpr int C = D / 8;
 #pragma unroll
   for (int it = 0; it < KStage<D>::kChunks; ++it) {
     const int c = it * kThreads + threadIdx.x;
-    st.r[it] = *reinterpret_cast<const u32x4*>(g + (size_t)(c / C) * D + (c % C) * 8);
+    const int row = min(c / C, rows - 1);
+    st.r[it] = *reinterpret_cast<const u32x4*>(g + (size_t)row * D + (c % C) * 8);
   }
 }
 
@@ -80,9 +83,10 @@ __device__ __forceinline__ void kstage_store(const KStage<D>& st, __bf16* lds) {
 
 // Whole-tile copy (load + store) for kernels that do not pipeline.
 template <int D>
-__device__ __forceinline__ void stage_ktile(const __bf16* __restrict__ g, __bf16* lds) {
+__device__ __forceinline__ void stage_ktile(const __bf16* __restrict__ g, __bf16* lds,
+                                            int rows = kBlock) {
   KStage<D> st;
-  kstage_load<D>(g, st);
+  kstage_load<D>(g, st, rows);
   kstage_store<D>(st, lds);
 }
 
@@ -331,6 +335,31 @@ __device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf
   for (int it = 0; it < INSTS; ++it) {
     const int blk_row = (it * NW + w) * ROWS;
     lds_dma16(g + (size_t)blk_row * D, voff, lbase + (uint32_t)(it * NW * ROWS * D * 2));
+  }
+}
+
+// The same copy for a partial tile (the last block of a sequence whose length
+// 128 does not divide): only `rows` (1..127) rows exist at g; every LDS row
+// past them receives a copy of row rows-1, so no address beyond the tile's
+// last token is formed.  The source row now varies per instruction, so the
+// per-lane offset is recomputed each time from the unchanged scalar base.
+template <int D, bool IS_V, int NW = kWaves>
+__device__ __forceinline__ void tile_load_lds_rows(const __bf16* __restrict__ g, __bf16* lds,
+                                                   int rows) {
+  constexpr int C = D / 8;
+  constexpr int ROWS = 64 / C;
+  constexpr int INSTS = kBlock / ROWS / NW;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) % NW;
+  const int l = threadIdx.x & 63;
+  g = uniform_ptr(g);
+  const int row0 = w * ROWS + l / C;
+  const int logical = (l % C) ^ (IS_V ? vswz<D>(row0) : kswz<D>(row0));
+  const uint32_t lbase = lds_addr(lds) + (uint32_t)(w * ROWS * D * 2);
+#pragma unroll
+  for (int it = 0; it < INSTS; ++it) {
+    const int src = min((it * NW + w) * ROWS + l / C, rows - 1);
+    const uint32_t voff = (uint32_t)(src * D + logical * 8) * 2u;
+    lds_dma16(g, voff, lbase + (uint32_t)(it * NW * ROWS * D * 2));
   }
 }
 

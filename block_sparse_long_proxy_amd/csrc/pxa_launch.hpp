@@ -9,6 +9,10 @@ namespace pxa {
 
 constexpr int kBlockTokens = 128;   // block edge the kernels are built for
 
+// Blocks of a sequence of N tokens; the last one is partial when 128 does not
+// divide N (its missing rows are read as copies of token N-1 and never written).
+inline int num_blocks(int N) { return (N + kBlockTokens - 1) / kBlockTokens; }
+
 enum BudgetMode { kBudgetDynamic = 0, kBudgetFixed = 1, kBudgetRatio = 2 };
 
 struct LaunchArgs {

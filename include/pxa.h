@@ -16,8 +16,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Batch 1, causal prefill.  H query heads, Hkv KV heads, N tokens, head
- *    dimension d, block B = 128, nb = N / B key/query blocks, G proxies.
+ *  - Causal prefill of one sequence (pxa_prefill_batch: several, one after
+ *    another).  H query heads, Hkv KV heads, N tokens, head dimension d, block
+ *    B = 128, nb = ceil(N / B) key/query blocks (when B does not divide N the
+ *    last block is partial and every step uses the tokens it has), G proxies.
  *  - Query head h uses KV head h / (H / Hkv).  Proxy group g holds query heads
  *    [g*H/G, (g+1)*H/G) and the (contiguous) KV heads those use.
  *  - Q, O: bfloat16 [H][N][d]; K, V: bfloat16 [Hkv][N][d]; proxies Qbar, Kbar:
@@ -46,12 +48,12 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 5
+#define PXA_ABI_VERSION 6
 
 enum {
   PXA_OK = 0,
   PXA_EINVAL = -1,       /* inconsistent shape, grouping, gamma or scale     */
-  PXA_EUNSUPPORTED = -2, /* d not 64/128, block not 128, N % 128 != 0, N too big */
+  PXA_EUNSUPPORTED = -2, /* d not 64/128, block not 128, N too big              */
   PXA_ENULL = -3,        /* a required pointer is NULL                       */
   PXA_EALIGN = -4,       /* a pointer violates its alignment requirement    */
   PXA_EWORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes query */
@@ -62,7 +64,8 @@ enum {
 typedef struct pxa_config {
   int32_t num_heads;     /* H  >= 1                                              */
   int32_t num_kv_heads;  /* Hkv >= 1, H % Hkv == 0                               */
-  int32_t seq_len;       /* N, a multiple of 128, 128 <= N <= 524288             */
+  int32_t seq_len;       /* N, 1 <= N <= 524288; nb = ceil(N/128) blocks, the
+                            last one partial when 128 does not divide N          */
   int32_t head_dim;      /* d, 64 or 128                                         */
   int32_t block;         /* must be 128 (blog post section 2: 128x128 blocks)    */
   int32_t num_proxies;   /* G: H % G == 0 and (Hkv % G == 0 or G % Hkv == 0)     */
@@ -77,7 +80,8 @@ typedef struct pxa_config {
  * (leeon-k.github.io, section 2.2).  Scoring: score_stride s > 1 is the
  * sequence-level skip that section 5 credits for the low estimation cost,
  * read as scoring only every s-th query of a block (offsets s-1, 2s-1, ...,
- * B-1) against every key -- an approximation of the s = 1 scores.  Every
+ * B-1; a partial last block adds its last query) against every key -- an
+ * approximation of the s = 1 scores.  Every
  * entry point that takes a `const pxa_options*` reads NULL as
  * {PXA_BUDGET_DYNAMIC, 1, 0, 0, 1, 0}, the behaviour of the calls without _ex.
  * Attention: skip_threshold > 0 turns on the running-max skip of the BLASST
@@ -88,7 +92,7 @@ enum { PXA_BUDGET_DYNAMIC = 0, PXA_BUDGET_FIXED = 1, PXA_BUDGET_RATIO = 2 };
 typedef struct pxa_options {
   int32_t budget_mode;   /* PXA_BUDGET_*                                         */
   int32_t last_blocks;   /* DYNAMIC: m, 1 <= m <= min(nb, PXA_MAX_PROBE_BLOCKS):
-                            the masses average the last m*B queries              */
+                            the masses average every query of the last m blocks */
   int32_t fixed_blocks;  /* FIXED: k >= 1, every head keeps min(k, I+1) ranked
                             blocks of row I (plus the diagonal)                  */
   float ratio;           /* RATIO: 0 < r <= 1, row I keeps ceil(r*(I+1)) ranked
@@ -158,16 +162,16 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q
                    void* stream);
 
 /* Several sequences in one call (batched prefill, equal or different
- * lengths).  Sequence s has seq_lens[s] tokens (host array; each a multiple of
- * 128 and at most cfg->seq_len, which sizes the workspace); its tensors are
+ * lengths).  Sequence s has seq_lens[s] tokens (host array; each in
+ * [1, cfg->seq_len], cfg->seq_len sizing the workspace); its tensors are
  * the usual per-sequence blocks Q/O [H][N_s][d], K/V [Hkv][N_s][d], stored one
  * after another (sequence s starts after the elements of sequences 0..s-1).
  * The whole method runs on each sequence in order on `stream` with the same
  * workspace (pxa_workspace_bytes_ex(cfg, opts)); the workspace keeps the
  * intermediates of the last sequence.  Each sequence's output equals what
- * pxa_prefill_ex gives for it alone.  PXA_EINVAL for num_seqs < 1 or a length
- * above cfg->seq_len, PXA_EUNSUPPORTED for a length that is not a multiple of
- * 128, PXA_ENULL for a NULL seq_lens. */
+ * pxa_prefill_ex gives for it alone.  PXA_EINVAL for num_seqs < 1, a length
+ * outside [1, cfg->seq_len] or a probe longer than a sequence, PXA_ENULL for a
+ * NULL seq_lens.  Every length is checked before the first launch. */
 int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t num_seqs,
                       const int32_t* seq_lens, const void* q, const void* k, const void* v,
                       void* o, void* ws, size_t ws_bytes, void* stream);
@@ -194,8 +198,9 @@ int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const voi
 
 /* Step 2, dynamic budget (section 4, step 2: the last query block estimates
  * each head's block-level sparsity; the abstract's "block-aware dynamic budget
- * estimation").  For head h: masses[h][J] = mean over the last B queries of
- * their exact causal softmax mass in key block J (fp32); k_h[h] = smallest k
+ * estimation").  For head h: masses[h][J] = mean over the queries of the last
+ * query block (B of them, fewer when it is partial) of their exact causal
+ * softmax mass in key block J (fp32); k_h[h] = smallest k
  * such that the masses of the first k blocks of the group's ranking of row
  * nb-1 (score descending, block ascending on ties) sum to >= gamma, else nb.
  * scores: as written by pxa_proxy_score.  ws: pxa_budget_workspace_bytes. */
@@ -203,7 +208,8 @@ int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k,
                         const float* scores, int32_t* k_h, float* masses,
                         void* ws, size_t ws_bytes, void* stream);
 /* Budget variants of step 2.  DYNAMIC with m probe blocks: as above with the
- * masses averaged over the last m*B queries (each over its own causal keys);
+ * masses averaged over every query of the last m blocks (each over its own
+ * causal keys);
  * ws: pxa_budget_workspace_bytes_ex.  FIXED: k_h[h] = fixed_blocks for every
  * head; only k_h is used (q, k, scores, masses, ws may be NULL).  RATIO has no
  * per-head budget: PXA_EINVAL. */
@@ -240,8 +246,11 @@ int pxa_block_select_ex(const pxa_config* cfg, const pxa_options* opts, const fl
 /* Block-sparse causal attention over the CSR mask (section 4, final step; the
  * attention of section 2).  o[h][i] = sum of softmax(scale * q.k_j) v_j over
  * the keys j <= i of the kept blocks of row (h, i / B), renormalised over
- * them; fp32 online softmax, bf16 MFMA products, bf16 output (RNE).  Entries
- * of a row outside [0, I] are ignored; a row with no valid entry yields zeros.
+ * them; fp32 online softmax, bf16 MFMA products, bf16 output (RNE).  Columns
+ * of a row must be ascending (as pxa_block_select writes them; otherwise the
+ * output is unspecified, though every memory access stays inside the tensors).
+ * Entries of a row outside [0, I] are ignored; a row with no valid entry yields
+ * zeros.
  * row_order (may be NULL): the order in which rows are handed to the GPU, a
  * permutation of [0, H*nb) such as pxa_block_select writes (entries outside
  * that range are skipped; a repeated row is computed twice with the same

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 5
+    assert pxa.pxa_abi_version() == 6
 
 
 def test_struct_layouts_match_header():
@@ -129,8 +129,10 @@ def test_batch_entry_point_validates_before_launch():
     _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, None, [], A, A, A, A, A, ws_bytes=big, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, None, [256, 2048], A, A, A, A, A,
             ws_bytes=big, stream=0)                 # longer than cfg.seq_len
-    _expect(B.PXA_EUNSUPPORTED, pxa.pxa_prefill_batch, cfg, None, [256, 200], A, A, A, A, A,
-            ws_bytes=big, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, None, [256, 0], A, A, A, A, A,
+            ws_bytes=big, stream=0)                 # an empty sequence
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, pxa.Options.dynamic(2), [1024, 100],
+            A, A, A, A, A, ws_bytes=1 << 40, stream=0)   # 100 tokens: one (partial) block < 2
     _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, pxa.Options.dynamic(4), [1024, 256],
             A, A, A, A, A, ws_bytes=1 << 40, stream=0)   # probe of 4 blocks > 2 blocks
     _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_batch, cfg, None, [256], A, A, A, A, A,
@@ -183,7 +185,9 @@ def test_budget_entry_points_validate_before_launch():
     (dict(head_dim=96), B.PXA_EUNSUPPORTED),
     (dict(head_dim=64), B.PXA_OK),
     (dict(block=64), B.PXA_EUNSUPPORTED),
-    (dict(seq_len=1000), B.PXA_EUNSUPPORTED),
+    (dict(seq_len=1000), B.PXA_OK),                  # partial last block of 104 tokens
+    (dict(seq_len=1), B.PXA_OK),
+    (dict(seq_len=0), B.PXA_EINVAL),
     (dict(seq_len=128), B.PXA_OK),
     (dict(seq_len=1 << 20), B.PXA_EUNSUPPORTED),
 ])
@@ -287,3 +291,21 @@ def test_product_path_does_not_import_oracle():
                 with open(os.path.join(dirpath, fn)) as f:
                     src = f.read()
                 assert "oracle" not in src.replace("oracle_", ""), fn
+
+
+def test_partial_last_block_sizes():
+    # N = 1000: nb = ceil(1000 / 128) = 8 blocks, the last of 104 tokens
+    cfg = _good(seq_len=1000)
+    assert cfg.nb == 8
+    H, G, N, d, nb = 8, 2, 1000, 128, 8
+    L = pxa.pxa_get_workspace_layout(cfg)
+    assert L.kbar - L.qbar >= G * N * d * 2 and L.scores - L.kbar >= G * N * d * 2
+    assert L.masses - L.scores >= G * nb * nb * 4
+    assert pxa.pxa_max_col_entries(cfg) == H * nb * (nb + 1) // 2
+    assert pxa.pxa_budget_workspace_bytes(cfg) >= H * nb * 128 * 4
+    assert pxa.pxa_select_workspace_bytes(cfg) >= H * nb * 4
+    # a probe may take all 8 blocks, the partial one included, but not 9
+    assert pxa.pxa_validate_options(cfg, pxa.Options.dynamic(8)) == B.PXA_OK
+    assert pxa.pxa_validate_options(cfg, pxa.Options.dynamic(9)) == B.PXA_EINVAL
+    one = _good(seq_len=5)
+    assert one.nb == 1 and pxa.pxa_max_col_entries(one) == H
