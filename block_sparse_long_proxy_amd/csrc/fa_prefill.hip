@@ -77,10 +77,11 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], float mx, bf16x8 
 // One pipeline step on key block J (tiles already in LDS / landing): S, the
 // softmax, then O += V P, issuing the copies of block Jn (knext / vnext NULL:
 // none; next_rows < 128: Jn is a partial last block).
-// skip_delta (raw logit units, -inf: off): the running-max skip of the
-// BLASST pages -- when every query of the wave has its tile max below
-// m_run + skip_delta, the wave drops the tile's softmax and PV product.
-template <int D, bool DIAG>
+// SKIP: the running-max skip of the BLASST pages -- when every query of the
+// wave has its tile max below m_run + skip_delta (raw logit units), the wave
+// drops the tile's softmax and PV product.  It is a template parameter so the
+// kernels launched without a threshold carry none of its code.
+template <int D, bool DIAG, bool SKIP>
 __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_lds, __bf16* ks,
                                         __bf16* vs, const bf16x8 (&qf)[D / 16],
                                         f32x16 (&oacc)[D / 32], float& m_run, float& l_run,
@@ -118,7 +119,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
   bf16x8 pb[4][2];
   const float mx = tile_row_max(s);
   // m_run is -inf only before the first tile, where the comparison is false
-  const bool skip = !DIAG && __all(mx < m_run + skip_delta);
+  const bool skip = SKIP && !DIAG && __all(mx < m_run + skip_delta);
   if (!skip) softmax_update<D>(s, mx, pb, oacc, m_run, l_run, scale_log2);
 
   wait_vmem();                   // this thread's part of V(J) has landed
@@ -146,7 +147,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
   }
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SKIP>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   if (J == I) {
     --it;
     const int Jn = next_block(it);
-    fa_step<D, true>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
+    fa_step<D, true, SKIP>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                      Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
                      Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr,
                      Jn >= 0 ? rows_of(Jn) : kBlock, skip_delta);
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   while (J >= 0) {
     --it;
     const int Jn = next_block(it);
-    fa_step<D, false>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
+    fa_step<D, false, SKIP>(ks, vs, ks, vs, qf, oacc, m_run, l_run, scale_log2, qloc,
                       Jn >= 0 ? kbase + (size_t)Jn * kTile : nullptr,
                       Jn >= 0 ? vbase + (size_t)Jn * kTile : nullptr,
                       Jn >= 0 ? rows_of(Jn) : kBlock, skip_delta);
@@ -288,15 +289,20 @@ static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, c
   const dim3 grid(a.H * num_blocks(a.N)), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   // skip when scale * (tile max - running max) < ln(threshold)
-  const float skip_delta = a.skip_threshold > 0.f ? std::log(a.skip_threshold) / a.scale : -INFINITY;
-  if (dense)
-    hipLaunchKernelGGL((fa_prefill_kernel<D, true>), grid, block, 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2, skip_delta);
-  else
-    hipLaunchKernelGGL((fa_prefill_kernel<D, false>), grid, block, 0, stream,
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, row_ptr, col_idx,
-                       row_order, (__bf16*)o, a.H, a.Hkv, a.N, sl2, skip_delta);
+  const bool skip = a.skip_threshold > 0.f;
+  const float skip_delta = skip ? std::log(a.skip_threshold) / a.scale : -INFINITY;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)q, (const __bf16*)k,
+                       (const __bf16*)v, row_ptr, col_idx, row_order, (__bf16*)o, a.H, a.Hkv, a.N,
+                       sl2, skip_delta);
+  };
+  if (dense) {
+    if (skip) go(fa_prefill_kernel<D, true, true>);
+    else go(fa_prefill_kernel<D, true, false>);
+  } else {
+    if (skip) go(fa_prefill_kernel<D, false, true>);
+    else go(fa_prefill_kernel<D, false, false>);
+  }
   return hipGetLastError();
 }
 
