@@ -44,10 +44,17 @@ def parse():
     ap.add_argument("--budget", default="dynamic:1",
                     help="budget variant: dynamic:M (probe the last M query blocks; the method's "
                          "own budget, M=1 by default), fixed:K or ratio:R")
+    ap.add_argument("--seq-len", type=int, default=None,
+                    help="override the workload's N (any length >= 1; when 128 does not divide "
+                         "it the last block is partial)")
+    ap.add_argument("--batch-lens", default=None,
+                    help="comma-separated sequence lengths: time one pxa_prefill_batch call over "
+                         "them (heads, dims, proxies and gamma of --workload) against one "
+                         "pxa_prefill_ex call per sequence, and print that line instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sdpa", action="store_true",
                     help="skip the context timing of torch's flash SDPA at the same shape")
-    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0,
                     help="approximate CPU seconds for the oracle sample")
     ap.add_argument("--profile", action="store_true",
                     help="short pass for hardware counters: one 256 MiB device copy (counter "
@@ -182,6 +189,81 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_k
     }
 
 
+def bench_batch(a, wl):
+    """Several sequences of the workload's layer shape in one pxa_prefill_batch
+    call (stored one after another), timed against one pxa_prefill_ex call per
+    sequence on the same buffers."""
+    import dataclasses
+    import numpy as np
+    import torch
+    import block_sparse_long_proxy_amd as pxa
+    from synth import generate
+
+    lens = [int(t) for t in a.batch_lens.split(",") if t]
+    gamma = a.gamma if a.gamma is not None else wl.gamma
+    H, Hkv, d, G = wl.num_heads, wl.num_kv_heads, wl.head_dim, wl.num_proxies
+    cfg = pxa.Config(H, Hkv, max(lens), d, G, gamma)
+    opts = dataclasses.replace(pxa.Options.dynamic(), score_stride=a.score_stride,
+                               skip_threshold=a.skip_threshold)
+    log(f"generating {len(lens)} sequences of {wl.name}'s shape: {lens}")
+    xs = [generate(wl.with_(name=f"{wl.name}_seq{i}", seq_len=n, seed=wl.seed + 1000 + i,
+                            n_needles=min(n, wl.n_needles))) for i, n in enumerate(lens)]
+    flat = {n: torch.cat([torch.from_numpy(x[n].view(np.int16)).view(torch.bfloat16).reshape(-1)
+                          for x in xs]).cuda() for n in ("q", "k", "v")}
+    del xs
+    o = torch.empty_like(flat["q"])
+    ws = torch.empty(pxa.pxa_workspace_bytes_ex(cfg, opts), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def batched():
+        pxa.pxa_prefill_batch(cfg, opts, lens, flat["q"], flat["k"], flat["v"], o, ws)
+
+    views = []
+    qo = ko = 0
+    for n in lens:
+        c = pxa.Config(H, Hkv, n, d, G, gamma)
+        views.append((c, flat["q"][qo:qo + H * n * d], flat["k"][ko:ko + Hkv * n * d],
+                      flat["v"][ko:ko + Hkv * n * d], o[qo:qo + H * n * d]))
+        qo += H * n * d
+        ko += Hkv * n * d
+
+    def one_by_one():
+        for c, q, k, v, oo in views:
+            pxa.pxa_prefill_ex(c, opts, q, k, v, oo, ws)
+
+    def timed(fn):
+        for _ in range(a.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(a.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / a.steps
+
+    ms_batch = timed(batched)
+    ob = o.clone()
+    ms_single = timed(one_by_one)
+    same = bool(torch.equal(ob, o))
+    log(f"batch {ms_batch:.3f} ms, one call per sequence {ms_single:.3f} ms, identical {same}")
+    tokens = sum(lens)
+    print(json.dumps({
+        "metric": "batched ProxyAttn prefill (pxa_prefill_batch) ms per call",
+        "value": round(ms_batch, 3), "unit": "ms", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_batch, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded generator, bf16, inputs resident in HBM)",
+        "config": {"workload": f"{len(lens)} sequences of the {wl.name} layer shape",
+                   "num_heads": H, "num_kv_heads": Hkv, "head_dim": d, "num_proxies": G,
+                   "gamma": gamma, "seq_lens": lens, "score_stride": a.score_stride},
+        "tokens": tokens, "tokens_per_s": round(tokens / (ms_batch * 1e-3), 1),
+        "one_call_per_sequence_ms": round(ms_single, 3),
+        "outputs_identical_to_one_call_per_sequence": same,
+    }), flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -195,6 +277,11 @@ def main():
     from synth import get_config, generate, input_digest
 
     wl = get_config(a.workload)
+    if a.batch_lens:
+        return bench_batch(a, wl)
+    if a.seq_len is not None:
+        wl = wl.with_(seq_len=a.seq_len, n_needles=min(a.seq_len, wl.n_needles),
+                      description=f"{wl.description} with N={a.seq_len}")
     gamma = a.gamma if a.gamma is not None else wl.gamma
     cfg = pxa.Config(wl.num_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.num_proxies, gamma)
     H, Hkv, N, d, G, nb = cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim, cfg.num_proxies, cfg.nb

@@ -35,7 +35,7 @@ class WorkloadConfig:
 
     @property
     def nb(self) -> int:
-        return self.seq_len // self.block
+        return -(-self.seq_len // self.block)     # the last block may be partial
 
     def with_(self, **kw) -> "WorkloadConfig":
         return replace(self, **kw)
