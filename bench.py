@@ -191,8 +191,9 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_k
 
 def bench_batch(a, wl):
     """Several sequences of the workload's layer shape in one pxa_prefill_batch
-    call (stored one after another), timed against one pxa_prefill_ex call per
-    sequence on the same buffers."""
+    call (stored one after another, fused workspace), timed against one
+    pxa_prefill_ex call per sequence on the same buffers and against the batch
+    call in a workspace for one sequence (sequences in turn)."""
     import dataclasses
     import numpy as np
     import torch
@@ -212,11 +213,17 @@ def bench_batch(a, wl):
                           for x in xs]).cuda() for n in ("q", "k", "v")}
     del xs
     o = torch.empty_like(flat["q"])
-    ws = torch.empty(pxa.pxa_workspace_bytes_ex(cfg, opts), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(pxa.pxa_batch_workspace_bytes(cfg, opts, lens), dtype=torch.uint8,
+                     device="cuda")
+    single_bytes = pxa.pxa_workspace_bytes_ex(cfg, opts)
     stream = torch.cuda.current_stream()
 
-    def batched():
+    def batched():        # fused: one set of launches per group of sequences
         pxa.pxa_prefill_batch(cfg, opts, lens, flat["q"], flat["k"], flat["v"], o, ws)
+
+    def batched_seq():    # a workspace for one sequence: the call runs them in turn
+        pxa.pxa_prefill_batch(cfg, opts, lens, flat["q"], flat["k"], flat["v"], o, ws,
+                              ws_bytes=single_bytes)
 
     views = []
     qo = ko = 0
@@ -247,7 +254,9 @@ def bench_batch(a, wl):
     ob = o.clone()
     ms_single = timed(one_by_one)
     same = bool(torch.equal(ob, o))
-    log(f"batch {ms_batch:.3f} ms, one call per sequence {ms_single:.3f} ms, identical {same}")
+    ms_seq = timed(batched_seq) if single_bytes < ws.numel() else None
+    log(f"fused batch {ms_batch:.3f} ms, one call per sequence {ms_single:.3f} ms, "
+        f"batch in a one-sequence workspace {ms_seq}, identical {same}")
     tokens = sum(lens)
     print(json.dumps({
         "metric": "batched ProxyAttn prefill (pxa_prefill_batch) ms per call",
@@ -260,6 +269,9 @@ def bench_batch(a, wl):
                    "gamma": gamma, "seq_lens": lens, "score_stride": a.score_stride},
         "tokens": tokens, "tokens_per_s": round(tokens / (ms_batch * 1e-3), 1),
         "one_call_per_sequence_ms": round(ms_single, 3),
+        "batch_in_one_sequence_workspace_ms": None if ms_seq is None else round(ms_seq, 3),
+        "speedup_vs_one_call_per_sequence": round(ms_single / ms_batch, 3),
+        "workspace_bytes": {"fused": int(ws.numel()), "one_sequence": int(single_bytes)},
         "outputs_identical_to_one_call_per_sequence": same,
     }), flush=True)
 

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     pxa_validate_options, pxa_proxy_score_ex, pxa_workspace_bytes_ex, pxa_get_workspace_layout_ex,
     pxa_budget_workspace_bytes_ex, pxa_prefill_ex, pxa_budget_estimate_ex, pxa_block_select_ex,
     pxa_sparse_prefill_ex, pxa_dense_prefill_ex, pxa_prefill_batch,
+    pxa_batch_workspace_bytes, pxa_get_batch_workspace_layout,
 )
 
 

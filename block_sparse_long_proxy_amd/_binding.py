@@ -45,6 +45,7 @@ PXA_BUDGET_DYNAMIC = 0
 PXA_BUDGET_FIXED = 1
 PXA_BUDGET_RATIO = 2
 PXA_MAX_PROBE_BLOCKS = 64
+PXA_MAX_FUSED_SEQS = 64
 
 
 class pxa_options(ctypes.Structure):
@@ -91,6 +92,11 @@ _SIGNATURES = {
     "pxa_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_budget_estimate_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_block_select_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_batch_workspace_bytes": (ctypes.c_size_t, [_CFG, _OPT, ctypes.c_int32,
+                                                    ctypes.POINTER(ctypes.c_int32)]),
+    "pxa_get_batch_workspace_layout": (ctypes.c_int, [_CFG, _OPT, ctypes.c_int32,
+                                                      ctypes.POINTER(ctypes.c_int32),
+                                                      ctypes.POINTER(pxa_workspace_layout)]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -384,13 +390,33 @@ def pxa_dense_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, strea
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill_ex")
 
 
+def _lens(seq_lens):
+    n = len(seq_lens)
+    return n, ((ctypes.c_int32 * max(n, 1))(*[int(x) for x in seq_lens]) if n else None)
+
+
+def pxa_batch_workspace_bytes(cfg: Config, opts: Optional[Options], seq_lens) -> int:
+    n, arr = _lens(seq_lens)
+    return load_library().pxa_batch_workspace_bytes(ctypes.byref(cfg.c()), _bref(opts), n, arr)
+
+
+def pxa_get_batch_workspace_layout(cfg: Config, opts: Optional[Options],
+                                   seq_lens) -> pxa_workspace_layout:
+    n, arr = _lens(seq_lens)
+    out = pxa_workspace_layout()
+    _check(load_library().pxa_get_batch_workspace_layout(ctypes.byref(cfg.c()), _bref(opts), n,
+                                                         arr, ctypes.byref(out)),
+           "pxa_get_batch_workspace_layout")
+    return out
+
+
 def pxa_prefill_batch(cfg: Config, opts: Optional[Options], seq_lens, q, k, v, o, ws,
                       ws_bytes=None, stream=None) -> None:
     """seq_lens: host list of per-sequence token counts; q/k/v/o: the per-sequence
-    [heads][N_s][d] blocks stored one after another (flat bf16 tensors are fine)."""
-    n = len(seq_lens)
-    arr = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in seq_lens])
+    [heads][N_s][d] blocks stored one after another (flat bf16 tensors are fine).
+    Fused when ws holds pxa_batch_workspace_bytes, else one sequence at a time."""
+    n, arr = _lens(seq_lens)
     _check(load_library().pxa_prefill_batch(
-        ctypes.byref(cfg.c()), _bref(opts), n, arr if n else None, _tp(q, "bf16", "q"),
+        ctypes.byref(cfg.c()), _bref(opts), n, arr, _tp(q, "bf16", "q"),
         _tp(k, "bf16", "k"), _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"),
         _nbytes(ws, ws_bytes), _stream(stream)), "pxa_prefill_batch")

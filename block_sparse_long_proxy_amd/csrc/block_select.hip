@@ -13,6 +13,9 @@
 //     row_ptr) are known without sorting.
 //   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr, and
 //     the XCD-aware, longest-first schedule of the rows -> row_order.
+// A fused batch has one CSR over the rows of all its sequences (sequence s's
+// rows follow those of the sequences before it), so the scan and the
+// schedule balance the XCDs over the whole batch.
 //   select_emit_kernel : one workgroup per (g, I); bitonic sort of the row's
 //     64-bit (score, index) keys in LDS gives every block's rank; each head
 //     of the group then compacts {J : rank < k or J == I} in ascending J.
@@ -41,12 +44,17 @@ __device__ __forceinline__ int row_budget(const int32_t* __restrict__ k_h, int h
 __global__ __launch_bounds__(256) void select_count_kernel(const float* __restrict__ scores,
                                                            const int32_t* __restrict__ k_h,
                                                            int32_t* __restrict__ counts, int H,
-                                                           int G, int nb, float ratio) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // g * nb + I
+                                                           int G, float ratio, const SeqTable t) {
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);   // G * blk[sid] + g * nb + I
   const int l = threadIdx.x & 63;
-  if (row >= G * nb) return;
+  if (gr >= G * t.blk[t.n]) return;
+  const int sid = t.n == 1 ? 0 : seq_find(t.blk, t.n, gr / G);
+  const int nb = t.blk[sid + 1] - t.blk[sid];
+  const int row = gr - G * t.blk[sid];                 // g * nb + I in this sequence
   const int g = row / nb, I = row % nb;
-  const float* s = scores + (size_t)row * nb;
+  counts += (size_t)H * t.blk[sid];
+  if (k_h) k_h += (size_t)H * sid;
+  const float* s = scores + (size_t)G * t.sq[sid] + (size_t)row * nb;
   const uint64_t kd = rank_key(s[I], (uint32_t)I);
   int ahead = 0;
   for (int J = l; J < I; J += 64) ahead += rank_key(s[J], (uint32_t)J) < kd ? 1 : 0;
@@ -181,16 +189,22 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ k_h,
-    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int H, int G, int nb,
-    int Pmax, float ratio) {
+    const int32_t* __restrict__ row_ptr, int32_t* __restrict__ col_idx, int H, int G,
+    int Pmax, float ratio, const SeqTable st) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);          // [Pmax]
   uint16_t* rank = reinterpret_cast<uint16_t*>(keys + Pmax);   // [nb]
   __shared__ int wsum[kEmitThreads / 64];
 
-  // Heavy rows first: blockIdx.x -> (I descending, g).
-  const int I = nb - 1 - (int)(blockIdx.x / G);
-  const int g = (int)(blockIdx.x % G);
+  // Sequence of a fused batch; within it heavy rows first: (I descending, g).
+  const int sid = st.n == 1 ? 0 : seq_find(st.blk, st.n, (int)blockIdx.x / G);
+  const int bl = (int)blockIdx.x - G * st.blk[sid];
+  const int nb = st.blk[sid + 1] - st.blk[sid];
+  scores += (size_t)G * st.sq[sid];
+  if (k_h) k_h += (size_t)H * sid;
+  row_ptr += (size_t)H * st.blk[sid];       // this sequence's rows of the fused CSR
+  const int I = nb - 1 - bl / G;
+  const int g = bl % G;
   const int n = I + 1;
   int P = 1;
   while (P < n) P <<= 1;
@@ -245,31 +259,32 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
   }
 }
 
-size_t select_ws_bytes(const LaunchArgs& a) {   // row lengths + the longest-first order
-  return 2 * align_up((size_t)a.H * num_blocks(a.N) * sizeof(int32_t), 256);
+size_t select_ws_bytes(const LaunchArgs& a, const SeqTable& t) {   // row lengths + the order
+  return 2 * align_up((size_t)a.H * t.blk[t.n] * sizeof(int32_t), 256);
 }
 
-hipError_t launch_select(const LaunchArgs& a, const float* scores, const int32_t* k_h,
-                         int32_t* row_ptr, int32_t* col_idx, int32_t* row_order, void* ws,
-                         hipStream_t stream) {
-  const int nb = num_blocks(a.N);
+hipError_t launch_select(const LaunchArgs& a, const SeqTable& t, const float* scores,
+                         const int32_t* k_h, int32_t* row_ptr, int32_t* col_idx,
+                         int32_t* row_order, void* ws, hipStream_t stream) {
+  const int rows = a.H * t.blk[t.n];        // CSR rows of every sequence, one after another
+  const int nb = max_blocks(t);
   int32_t* counts = (int32_t*)ws;
-  int32_t* tmp = (int32_t*)((char*)ws + align_up((size_t)a.H * nb * sizeof(int32_t), 256));
-  hipLaunchKernelGGL(select_count_kernel, dim3((a.G * nb + 3) / 4), dim3(256), 0, stream, scores,
-                     k_h, counts, a.H, a.G, nb, a.ratio);
+  int32_t* tmp = (int32_t*)((char*)ws + align_up((size_t)rows * sizeof(int32_t), 256));
+  hipLaunchKernelGGL(select_count_kernel, dim3((a.G * t.blk[t.n] + 3) / 4), dim3(256), 0, stream,
+                     scores, k_h, counts, a.H, a.G, a.ratio, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_len = nb + 1;   // a row keeps at most I + 1 <= nb blocks
   hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads),
                      row_order ? (size_t)(max_len + 1) * sizeof(int) : 0, stream, counts, row_ptr,
-                     row_order, tmp, a.H * nb, max_len);
+                     row_order, tmp, rows, max_len);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   int Pmax = 1;
   while (Pmax < nb) Pmax <<= 1;
   const size_t smem = (size_t)Pmax * 8 + align_up((size_t)nb * 2, 16);
-  hipLaunchKernelGGL(select_emit_kernel, dim3(a.G * nb), dim3(kEmitThreads), smem, stream, scores,
-                     k_h, row_ptr, col_idx, a.H, a.G, nb, Pmax, a.ratio);
+  hipLaunchKernelGGL(select_emit_kernel, dim3(a.G * t.blk[t.n]), dim3(kEmitThreads), smem, stream,
+                     scores, k_h, row_ptr, col_idx, a.H, a.G, Pmax, a.ratio, t);
   return hipGetLastError();
 }
 

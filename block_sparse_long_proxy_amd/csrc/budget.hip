@@ -30,18 +30,23 @@ constexpr int kFinThreads = 512;
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, float* __restrict__ lse,
-    int H, int Hkv, int N, int m, float scale_log2) {
+    int H, int Hkv, int m, float scale_log2, const SeqTable t) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
-  const int nb = (N + kBlock - 1) / kBlock;
+  const int sid = (int)blockIdx.z / m;     // sequence of a fused batch
+  const int z = (int)blockIdx.z % m;       // probe block z of m
+  const int N = t.tok[sid + 1] - t.tok[sid];
+  const int nb = t.blk[sid + 1] - t.blk[sid];
+  q += (size_t)t.tok[sid] * H * D;
+  k += (size_t)t.tok[sid] * Hkv * D;
+  lse += (size_t)H * m * t.blk[sid] * kBlock;
   const int h = blockIdx.y;
-  const int z = blockIdx.z;                // probe block z of m
   const int kvh = h / (H / Hkv);
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int qloc = 32 * w + (l & 31);
   const int I = nb - m + z;                // its query block
 
-  const int j0 = blockIdx.x * kLseBlocksPerWG;
+  const int j0 = blockIdx.x * kLseBlocksPerWG;   // grid x covers the longest sequence
   const int j1 = min(I + 1, j0 + kLseBlocksPerWG);   // causal key blocks only
   if (j0 >= j1) return;
   bf16x8 qf[D / 16];
@@ -101,8 +106,17 @@ __device__ __forceinline__ void bitonic_sort_u64(uint64_t* keys, int P) {
 
 __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
     const float* __restrict__ lse, const float* __restrict__ scores, int32_t* __restrict__ k_h,
-    float* __restrict__ masses, int H, int G, int nb, int m, int P, float gamma, int tail) {
+    float* __restrict__ masses, int H, int G, int m, float gamma, const SeqTable st) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int sid = (int)blockIdx.x / H;     // sequence of a fused batch
+  const int nb = st.blk[sid + 1] - st.blk[sid];
+  const int tail = (st.tok[sid + 1] - st.tok[sid]) - (nb - 1) * kBlock;
+  lse += (size_t)H * m * st.blk[sid] * kBlock;
+  scores += (size_t)G * st.sq[sid];
+  masses += (size_t)H * st.blk[sid];
+  k_h += (size_t)H * sid;
+  int P = 1;                               // sort size: a power of two >= nb
+  while (P < nb) P <<= 1;
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);              // [P]
   float* mass = reinterpret_cast<float*>(keys + P);                 // [nb]
   float* qlse = mass + nb;                                          // [128]
@@ -111,7 +125,7 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
   float* csum = part_s + 4 * kBlock;                                // [kFinThreads]
   __shared__ int first_hit;
 
-  const int h = blockIdx.x;
+  const int h = (int)blockIdx.x % H;
   const int g = h / (H / G);
   const int t = threadIdx.x;
 
@@ -212,42 +226,44 @@ static int pow2_at_least(int n) {
   return p;
 }
 
-size_t budget_ws_bytes(const LaunchArgs& a) {   // lse [H][m][nb][128]
+size_t budget_ws_bytes(const LaunchArgs& a, const SeqTable& t) {   // lse [s][H][m][nb_s][128]
   const size_t m = a.budget_mode == kBudgetDynamic ? (size_t)a.last_blocks : 1;
-  return align_up((size_t)a.H * m * num_blocks(a.N) * kBlock * sizeof(float), 256);
+  return align_up((size_t)a.H * m * t.blk[t.n] * kBlock * sizeof(float), 256);
 }
 
-__global__ void budget_fixed_kernel(int32_t* __restrict__ k_h, int H, int k) {
-  for (int h = blockIdx.x * blockDim.x + threadIdx.x; h < H; h += gridDim.x * blockDim.x)
-    k_h[h] = k;
+__global__ void budget_fixed_kernel(int32_t* __restrict__ k_h, int n, int k) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    k_h[i] = k;
 }
 
-hipError_t launch_fixed_budget(const LaunchArgs& a, int32_t* k_h, hipStream_t stream) {
-  hipLaunchKernelGGL(budget_fixed_kernel, dim3((a.H + 255) / 256), dim3(256), 0, stream, k_h, a.H,
+hipError_t launch_fixed_budget(const LaunchArgs& a, const SeqTable& t, int32_t* k_h,
+                               hipStream_t stream) {
+  const int n = a.H * t.n;
+  hipLaunchKernelGGL(budget_fixed_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, k_h, n,
                      a.fixed_blocks);
   return hipGetLastError();
 }
 
-hipError_t launch_budget(const LaunchArgs& a, const void* q, const void* k, const float* scores,
-                         int32_t* k_h, float* masses, void* ws, hipStream_t stream) {
-  const int nb = num_blocks(a.N);
-  const int tail = a.N - (nb - 1) * kBlock;
+hipError_t launch_budget(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,
+                         const float* scores, int32_t* k_h, float* masses, void* ws,
+                         hipStream_t stream) {
+  const int nb = max_blocks(t);
   float* lse = (float*)ws;
   const float sl2 = a.scale * kLog2e;
   const int m = a.last_blocks;
-  const dim3 g1((nb + kLseBlocksPerWG - 1) / kLseBlocksPerWG, a.H, m);
+  const dim3 g1((nb + kLseBlocksPerWG - 1) / kLseBlocksPerWG, a.H, m * t.n);
   if (a.D == 64)
     hipLaunchKernelGGL(budget_lse_kernel<64>, g1, dim3(kThreads), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, m, sl2);
+                       (const __bf16*)k, lse, a.H, a.Hkv, m, sl2, t);
   else
     hipLaunchKernelGGL(budget_lse_kernel<128>, g1, dim3(kThreads), 0, stream, (const __bf16*)q,
-                       (const __bf16*)k, lse, a.H, a.Hkv, a.N, m, sl2);
+                       (const __bf16*)k, lse, a.H, a.Hkv, m, sl2, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int P = pow2_at_least(nb);
+  const int P = pow2_at_least(nb);   // LDS for the longest sequence
   const size_t smem = (size_t)P * 8 + (size_t)nb * 4 + (size_t)kBlock * 4 * 9 + kFinThreads * 4;
-  hipLaunchKernelGGL(budget_finalize_kernel, dim3(a.H), dim3(kFinThreads), smem, stream, lse,
-                     scores, k_h, masses, a.H, a.G, nb, m, P, a.gamma, tail);
+  hipLaunchKernelGGL(budget_finalize_kernel, dim3(a.H * t.n), dim3(kFinThreads), smem, stream, lse,
+                     scores, k_h, masses, a.H, a.G, m, a.gamma, t);
   return hipGetLastError();
 }
 

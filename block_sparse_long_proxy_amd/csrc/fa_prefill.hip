@@ -151,19 +151,26 @@ template <int D, bool DENSE, bool SKIP>
 __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col_idx,
-    const int32_t* __restrict__ row_order, __bf16* __restrict__ o, int H, int Hkv, int N,
-    float scale_log2, float skip_delta) {
+    const int32_t* __restrict__ row_order, __bf16* __restrict__ o, int H, int Hkv,
+    float scale_log2, float skip_delta, const SeqTable t) {
   __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];   // K tile, kswz layout
   __shared__ __attribute__((aligned(16))) __bf16 vs[kBlock * D];   // V tile, vswz layout
 
-  const int nb = (N + kBlock - 1) / kBlock;
-  int h, I;
+  // Rows of a fused batch are numbered sequence by sequence (H * nb_s rows
+  // each, h * nb_s + I within the sequence).
+  int sid, h, I, nb;
   if (!DENSE && row_order) {
     const int r = row_order[blockIdx.x];
-    if (r < 0 || r >= H * nb) return;
-    h = r / nb;
-    I = r % nb;
+    if (r < 0 || r >= H * t.blk[t.n]) return;
+    sid = t.n == 1 ? 0 : seq_find(t.blk, t.n, r / H);
+    nb = t.blk[sid + 1] - t.blk[sid];
+    const int rr = r - H * t.blk[sid];
+    h = rr / nb;
+    I = rr % nb;
   } else {
+    sid = t.n == 1 ? 0 : seq_find(t.blk, t.n, (int)blockIdx.x / H);
+    nb = t.blk[sid + 1] - t.blk[sid];
+    const int bl = (int)blockIdx.x - H * t.blk[sid];
     // Query blocks from last (longest causal row) to first.  Workgroups are
     // dealt round-robin to the 8 XCDs (XCD = blockIdx mod 8).  Dense: XCD x
     // gets the consecutive heads [x H/8, (x+1) H/8), i.e. whole KV-head groups
@@ -171,9 +178,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     // the same time share that XCD's L2.  Sparse without a schedule: heads
     // have unequal work, so the head index is rotated by the query block and
     // every head visits every XCD.
-    const int step = (int)(blockIdx.x / H);
+    const int step = bl / H;
     I = nb - 1 - step;
-    const int j = (int)(blockIdx.x % H);
+    const int j = bl % H;
     if (DENSE)
       h = (H % 8 == 0) ? (j % 8) * (H / 8) + j / 8 : j;
     else
@@ -183,6 +190,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
   h = __builtin_amdgcn_readfirstlane(h);
   I = __builtin_amdgcn_readfirstlane(I);
   const int kvh = __builtin_amdgcn_readfirstlane(h / (H / Hkv));
+  const int N = t.tok[sid + 1] - t.tok[sid];
+  const size_t tok0 = (size_t)t.tok[sid];
+  q += tok0 * H * D;
+  o += tok0 * H * D;
+  k += tok0 * Hkv * D;
+  v += tok0 * Hkv * D;
+  const int row = H * t.blk[sid] + h * nb + I;   // CSR row
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int qloc = 32 * w + (l & 31);          // query index inside block I
@@ -209,8 +223,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
     beg = 0;
     end = I + 1;
   } else {
-    beg = row_ptr[h * nb + I];
-    end = row_ptr[h * nb + I + 1];
+    beg = row_ptr[row];
+    end = row_ptr[row + 1];
   }
   // Next valid block at or below list position `it` (walking towards beg),
   // or -1.  The list is visited from its end: the diagonal block, the largest
@@ -283,18 +297,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa_prefill_kernel(
 }
 
 template <int D>
-static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, const void* v,
-                            const int32_t* row_ptr, const int32_t* col_idx,
+static hipError_t launch_fa(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,
+                            const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                             const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
-  const dim3 grid(a.H * num_blocks(a.N)), block(kThreads);
+  const dim3 grid(a.H * t.blk[t.n]), block(kThreads);
   const float sl2 = a.scale * kLog2e;
   // skip when scale * (tile max - running max) < ln(threshold)
   const bool skip = a.skip_threshold > 0.f;
   const float skip_delta = skip ? std::log(a.skip_threshold) / a.scale : -INFINITY;
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)q, (const __bf16*)k,
-                       (const __bf16*)v, row_ptr, col_idx, row_order, (__bf16*)o, a.H, a.Hkv, a.N,
-                       sl2, skip_delta);
+                       (const __bf16*)v, row_ptr, col_idx, row_order, (__bf16*)o, a.H, a.Hkv,
+                       sl2, skip_delta, t);
   };
   if (dense) {
     if (skip) go(fa_prefill_kernel<D, true, true>);
@@ -306,11 +320,11 @@ static hipError_t launch_fa(const LaunchArgs& a, const void* q, const void* k, c
   return hipGetLastError();
 }
 
-hipError_t launch_fa_prefill(const LaunchArgs& a, const void* q, const void* k, const void* v,
-                             const int32_t* row_ptr, const int32_t* col_idx,
+hipError_t launch_fa_prefill(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,
+                             const void* v, const int32_t* row_ptr, const int32_t* col_idx,
                              const int32_t* row_order, void* o, bool dense, hipStream_t stream) {
-  return a.D == 64 ? launch_fa<64>(a, q, k, v, row_ptr, col_idx, row_order, o, dense, stream)
-                   : launch_fa<128>(a, q, k, v, row_ptr, col_idx, row_order, o, dense, stream);
+  return a.D == 64 ? launch_fa<64>(a, t, q, k, v, row_ptr, col_idx, row_order, o, dense, stream)
+                   : launch_fa<128>(a, t, q, k, v, row_ptr, col_idx, row_order, o, dense, stream);
 }
 
 }  // namespace pxa

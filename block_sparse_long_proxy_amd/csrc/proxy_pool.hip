@@ -8,7 +8,9 @@
 //
 // Pure streaming: every thread owns one 16-byte chunk (8 dims of one token)
 // of one proxy, sums the member heads' chunks in fp32 in head order, divides
-// by the member count and rounds once to bf16.
+// by the member count and rounds once to bf16.  Grid z covers (sequence,
+// Q or K) of a fused batch; each sequence's tensors start after the previous
+// ones.
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -16,11 +18,14 @@ namespace pxa {
 
 __global__ __launch_bounds__(256) void proxy_pool_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, __bf16* __restrict__ qbar,
-    __bf16* __restrict__ kbar, int H, int Hkv, int G, size_t chunks_per_head, size_t head_elems) {
+    __bf16* __restrict__ kbar, int H, int Hkv, int G, int D, const SeqTable t) {
+  const int s = (int)(blockIdx.z >> 1);        // sequence
+  const bool is_k = (blockIdx.z & 1) != 0;
+  const size_t tok0 = (size_t)t.tok[s];
+  const size_t head_elems = (size_t)(t.tok[s + 1] - t.tok[s]) * D;
   const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= chunks_per_head) return;
+  if (c >= head_elems / 8) return;
   const int g = blockIdx.y;
-  const bool is_k = blockIdx.z != 0;
   const int qpg = H / G;                       // query heads per group
   int first, count;
   if (!is_k) {
@@ -31,7 +36,8 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(
     first = (g * qpg) / qpk;
     count = ((g + 1) * qpg - 1) / qpk - first + 1;
   }
-  const __bf16* src = (is_k ? k : q) + (size_t)first * head_elems + c * 8;
+  const __bf16* src = (is_k ? k + tok0 * Hkv * D : q + tok0 * H * D) +
+                      (size_t)first * head_elems + c * 8;
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -44,18 +50,16 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(
   bf16x8 out;
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] / n);
-  __bf16* dst = (is_k ? kbar : qbar) + (size_t)g * head_elems + c * 8;
+  __bf16* dst = (is_k ? kbar : qbar) + tok0 * G * D + (size_t)g * head_elems + c * 8;
   *reinterpret_cast<bf16x8*>(dst) = out;
 }
 
-hipError_t launch_proxy_pool(const LaunchArgs& a, const void* q, const void* k, void* qbar,
-                             void* kbar, hipStream_t stream) {
-  const size_t head_elems = (size_t)a.N * a.D;
-  const size_t chunks = head_elems / 8;
-  const dim3 grid((unsigned)((chunks + 255) / 256), a.G, 2), block(256);
+hipError_t launch_proxy_pool(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,
+                             void* qbar, void* kbar, hipStream_t stream) {
+  const size_t chunks = (size_t)max_len(t) * a.D / 8;   // of the longest sequence
+  const dim3 grid((unsigned)((chunks + 255) / 256), a.G, 2 * t.n), block(256);
   hipLaunchKernelGGL(proxy_pool_kernel, grid, block, 0, stream, (const __bf16*)q,
-                     (const __bf16*)k, (__bf16*)qbar, (__bf16*)kbar, a.H, a.Hkv, a.G, chunks,
-                     head_elems);
+                     (const __bf16*)k, (__bf16*)qbar, (__bf16*)kbar, a.H, a.Hkv, a.G, a.D, t);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ constexpr int kScoreBufs = 2;                  // K tile in use + the next one i
 template <int D, int STRIDE>
 __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
-    int G, int N, float scale) {
+    int G, float scale, const SeqTable t) {
   // STRIDE s: rows I0, I0-1, ..., I0-s+1 share the workgroup, each with its
   // 128/s scored queries (offsets s-1, 2s-1, ..., 127), so every wave still
   // holds 4 chunks of 32 queries and each K tile feeds the same MFMA work.
@@ -48,10 +48,18 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
   __shared__ float wm[2][R][kWaves][64];         // per-wave maxima of one 64-tile chunk
 
-  const int nb = (N + kBlock - 1) / kBlock;
+  // sequence of a fused batch (its workgroups are consecutive), then this
+  // sequence's proxies and score grid
+  const int sid = t.n == 1 ? 0 : seq_find(t.swg, t.n, (int)blockIdx.x);
+  const int bl = (int)blockIdx.x - t.swg[sid];
+  const int N = t.tok[sid + 1] - t.tok[sid];
+  qbar += (size_t)t.tok[sid] * G * D;
+  kbar += (size_t)t.tok[sid] * G * D;
+  scores += (size_t)G * t.sq[sid];
+  const int nb = t.blk[sid + 1] - t.blk[sid];
   const int tail = N - (nb - 1) * kBlock;        // tokens of the last block (128 unless partial)
-  const int g = (int)(blockIdx.x % G);
-  const int I0 = nb - 1 - R * (int)(blockIdx.x / G);   // top row; longest rows first
+  const int g = bl % G;
+  const int I0 = nb - 1 - R * (bl / G);          // top row; longest rows first
   const int ws = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // keys 32 ws ..
   const int l = threadIdx.x & 63;
   const int hi = l >> 5;
@@ -164,13 +172,12 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   store_chunk(I0 >> 6);
 }
 
-hipError_t launch_proxy_score(const LaunchArgs& a, const void* qbar, const void* kbar,
-                              float* scores, hipStream_t stream) {
-  const int nb = num_blocks(a.N);
-  const dim3 grid(a.G * ((nb + a.score_stride - 1) / a.score_stride)), block(kThreads);
+hipError_t launch_proxy_score(const LaunchArgs& a, const SeqTable& t, const void* qbar,
+                              const void* kbar, float* scores, hipStream_t stream) {
+  const dim3 grid(t.swg[t.n]), block(kThreads);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)qbar, (const __bf16*)kbar,
-                       scores, a.G, a.N, a.scale);
+                       scores, a.G, a.scale, t);
   };
   if (a.D == 64) {
     if (a.score_stride == 4) go(proxy_score_kernel<64, 4>);

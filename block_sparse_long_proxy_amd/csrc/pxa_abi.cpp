@@ -111,26 +111,112 @@ int hip_rc(hipError_t e) {
   return PXA_EHIP;
 }
 
-void layout_of(const pxa_config* c, const pxa_options* b, pxa_workspace_layout* L) {
-  const pxa::LaunchArgs a = args_of(c, b);
-  const size_t nb = (size_t)pxa::num_blocks(a.N);
+// Workspace parts of one set of launches over the sequences of t, each part
+// the concatenation of the sequences' own parts in order.
+void layout_of_table(const pxa::LaunchArgs& a, const pxa::SeqTable& t, pxa_workspace_layout* L) {
+  const size_t toks = (size_t)t.tok[t.n], blks = (size_t)t.blk[t.n], sq = (size_t)t.sq[t.n];
+  size_t tri = 0;   // causal blocks of one head, summed over the sequences
+  for (int s = 0; s < t.n; ++s) {
+    const size_t nb = (size_t)(t.blk[s + 1] - t.blk[s]);
+    tri += nb * (nb + 1) / 2;
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = pxa::align_up(off + bytes, 256);
     return o;
   };
-  L->qbar = take((size_t)a.G * a.N * a.D * 2);
-  L->kbar = take((size_t)a.G * a.N * a.D * 2);
-  L->scores = take((size_t)a.G * nb * nb * 4);
-  L->masses = take((size_t)a.H * nb * 4);
-  L->k_h = take((size_t)a.H * 4);
-  L->row_ptr = take(((size_t)a.H * nb + 1) * 4);
-  L->col_idx = take((size_t)a.H * nb * (nb + 1) / 2 * 4);
-  L->row_order = take((size_t)a.H * nb * 4);
-  L->budget_ws = take(pxa::budget_ws_bytes(a));
-  L->select_ws = take(pxa::select_ws_bytes(a));
+  L->qbar = take((size_t)a.G * toks * a.D * 2);
+  L->kbar = take((size_t)a.G * toks * a.D * 2);
+  L->scores = take((size_t)a.G * sq * 4);
+  L->masses = take((size_t)a.H * blks * 4);
+  L->k_h = take((size_t)a.H * t.n * 4);
+  L->row_ptr = take(((size_t)a.H * blks + 1) * 4);
+  L->col_idx = take((size_t)a.H * tri * 4);
+  L->row_order = take((size_t)a.H * blks * 4);
+  L->budget_ws = take(pxa::budget_ws_bytes(a, t));
+  L->select_ws = take(pxa::select_ws_bytes(a, t));
   L->total = off;
+}
+
+void layout_of(const pxa_config* c, const pxa_options* b, pxa_workspace_layout* L) {
+  const pxa::LaunchArgs a = args_of(c, b);
+  layout_of_table(a, pxa::one_seq(a), L);
+}
+
+// The whole method over the sequences of t on one stream (workspace laid out
+// by layout_of_table).
+int run_method(const pxa::LaunchArgs& a, const pxa::SeqTable& t, const void* q, const void* k,
+               const void* v, void* o, void* ws, const pxa_workspace_layout& L,
+               hipStream_t s) {
+  char* w = (char*)ws;
+  void* qbar = w + L.qbar;
+  void* kbar = w + L.kbar;
+  float* scores = (float*)(w + L.scores);
+  float* masses = (float*)(w + L.masses);
+  int32_t* k_h = (int32_t*)(w + L.k_h);
+  int32_t* row_ptr = (int32_t*)(w + L.row_ptr);
+  int32_t* col_idx = (int32_t*)(w + L.col_idx);
+  int32_t* row_order = (int32_t*)(w + L.row_order);
+  int rc;
+  if ((rc = hip_rc(pxa::launch_proxy_pool(a, t, q, k, qbar, kbar, s)))) return rc;
+  if ((rc = hip_rc(pxa::launch_proxy_score(a, t, qbar, kbar, scores, s)))) return rc;
+  if (a.budget_mode == pxa::kBudgetDynamic)
+    rc = hip_rc(pxa::launch_budget(a, t, q, k, scores, k_h, masses, w + L.budget_ws, s));
+  else if (a.budget_mode == pxa::kBudgetFixed)
+    rc = hip_rc(pxa::launch_fixed_budget(a, t, k_h, s));
+  if (rc) return rc;
+  const bool ratio = a.budget_mode == pxa::kBudgetRatio;
+  if ((rc = hip_rc(pxa::launch_select(a, t, scores, ratio ? nullptr : k_h, row_ptr, col_idx,
+                                      row_order, w + L.select_ws, s))))
+    return rc;
+  return hip_rc(pxa::launch_fa_prefill(a, t, q, k, v, row_ptr, col_idx, row_order, o, false, s));
+}
+
+// Groups of a batch fused into one set of launches: consecutive sequences,
+// at most kMaxFusedSeqs of them, with all CSR entries of a group addressable
+// by int32.  Calls f(first, count) for each group in order.
+template <typename F>
+void for_each_group(const pxa_config* c, int32_t n, const int32_t* lens, F&& f) {
+  int32_t first = 0;
+  while (first < n) {
+    int32_t cnt = 0;
+    int64_t entries = 0;
+    while (first + cnt < n && cnt < pxa::kMaxFusedSeqs) {
+      const int64_t nb = pxa::num_blocks(lens[first + cnt]);
+      const int64_t add = (int64_t)c->num_heads * nb * (nb + 1) / 2;
+      if (cnt > 0 && entries + add > INT32_MAX) break;
+      entries += add;
+      ++cnt;
+    }
+    f(first, cnt);
+    first += cnt;
+  }
+}
+
+// Lengths of a batch: every one valid for cfg and opts (PXA_OK) or the first error.
+int check_lengths(const pxa_config* cfg, const pxa_options* opts, int32_t n, const int32_t* lens) {
+  if (n < 1) return PXA_EINVAL;
+  if (!lens) return PXA_ENULL;
+  for (int32_t s = 0; s < n; ++s) {
+    if (lens[s] < 1 || lens[s] > cfg->seq_len) return PXA_EINVAL;
+    pxa_config c = *cfg;
+    c.seq_len = lens[s];
+    const int rc = check_all(&c, opts);   // e.g. a probe longer than this sequence
+    if (rc) return rc;
+  }
+  return PXA_OK;
+}
+
+size_t fused_bytes(const pxa_config* cfg, const pxa_options* opts, int32_t n, const int32_t* lens) {
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  size_t need = 0;
+  for_each_group(cfg, n, lens, [&](int32_t first, int32_t cnt) {
+    pxa_workspace_layout L;
+    layout_of_table(a, pxa::make_table(lens + first, cnt, a.G, a.score_stride), &L);
+    need = L.total > need ? L.total : need;
+  });
+  return need;
 }
 
 }  // namespace
@@ -173,12 +259,14 @@ int pxa_get_workspace_layout(const pxa_config* cfg, pxa_workspace_layout* out) {
 
 size_t pxa_budget_workspace_bytes(const pxa_config* cfg) {
   if (check_config(cfg) != PXA_OK) return 0;
-  return pxa::budget_ws_bytes(args_of(cfg));
+  const pxa::LaunchArgs a = args_of(cfg);
+  return pxa::budget_ws_bytes(a, pxa::one_seq(a));
 }
 
 size_t pxa_select_workspace_bytes(const pxa_config* cfg) {
   if (check_config(cfg) != PXA_OK) return 0;
-  return pxa::select_ws_bytes(args_of(cfg));
+  const pxa::LaunchArgs a = args_of(cfg);
+  return pxa::select_ws_bytes(a, pxa::one_seq(a));
 }
 
 size_t pxa_max_col_entries(const pxa_config* cfg) {
@@ -209,7 +297,8 @@ int pxa_get_workspace_layout_ex(const pxa_config* cfg, const pxa_options* budget
 
 size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* budget) {
   if (check_all(cfg, budget) != PXA_OK) return 0;
-  return pxa::budget_ws_bytes(args_of(cfg, budget));
+  const pxa::LaunchArgs a = args_of(cfg, budget);
+  return pxa::budget_ws_bytes(a, pxa::one_seq(a));
 }
 
 int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k, void* qbar, void* kbar,
@@ -217,7 +306,8 @@ int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k, void* qb
   int rc = check_config(cfg);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {qbar, 16}, {kbar, 16}}))) return rc;
-  return hip_rc(pxa::launch_proxy_pool(args_of(cfg), q, k, qbar, kbar, (hipStream_t)stream));
+  const pxa::LaunchArgs a = args_of(cfg);
+  return hip_rc(pxa::launch_proxy_pool(a, pxa::one_seq(a), q, k, qbar, kbar, (hipStream_t)stream));
 }
 
 int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const void* qbar,
@@ -225,7 +315,8 @@ int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const voi
   int rc = check_all(cfg, opts);
   if (rc) return rc;
   if ((rc = ptrs_ok({{qbar, 16}, {kbar, 16}, {scores, 4}}))) return rc;
-  return hip_rc(pxa::launch_proxy_score(args_of(cfg, opts), qbar, kbar, scores,
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  return hip_rc(pxa::launch_proxy_score(a, pxa::one_seq(a), qbar, kbar, scores,
                                         (hipStream_t)stream));
 }
 
@@ -243,11 +334,12 @@ int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_options* budget, con
   if (a.budget_mode == pxa::kBudgetRatio) return PXA_EINVAL;   // no per-head budget
   if (a.budget_mode == pxa::kBudgetFixed) {
     if ((rc = ptrs_ok({{k_h, 4}}))) return rc;
-    return hip_rc(pxa::launch_fixed_budget(a, k_h, (hipStream_t)stream));
+    return hip_rc(pxa::launch_fixed_budget(a, pxa::one_seq(a), k_h, (hipStream_t)stream));
   }
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {scores, 4}, {k_h, 4}, {masses, 4}, {ws, 256}}))) return rc;
-  if (ws_bytes < pxa::budget_ws_bytes(a)) return PXA_EWORKSPACE;
-  return hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, ws, (hipStream_t)stream));
+  const pxa::SeqTable t = pxa::one_seq(a);
+  if (ws_bytes < pxa::budget_ws_bytes(a, t)) return PXA_EWORKSPACE;
+  return hip_rc(pxa::launch_budget(a, t, q, k, scores, k_h, masses, ws, (hipStream_t)stream));
 }
 
 int pxa_budget_estimate(const pxa_config* cfg, const void* q, const void* k, const float* scores,
@@ -265,9 +357,10 @@ int pxa_block_select_ex(const pxa_config* cfg, const pxa_options* budget, const 
   if ((rc = ptrs_ok({{scores, 4}, {row_ptr, 4}, {col_idx, 4}, {ws, 256}}))) return rc;
   if (!ratio && (rc = ptrs_ok({{k_h, 4}}))) return rc;
   if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
-  if (ws_bytes < pxa::select_ws_bytes(a)) return PXA_EWORKSPACE;
-  return hip_rc(pxa::launch_select(a, scores, ratio ? nullptr : k_h, row_ptr, col_idx, row_order,
-                                   ws, (hipStream_t)stream));
+  const pxa::SeqTable t = pxa::one_seq(a);
+  if (ws_bytes < pxa::select_ws_bytes(a, t)) return PXA_EWORKSPACE;
+  return hip_rc(pxa::launch_select(a, t, scores, ratio ? nullptr : k_h, row_ptr, col_idx,
+                                   row_order, ws, (hipStream_t)stream));
 }
 
 int pxa_block_select(const pxa_config* cfg, const float* scores, const int32_t* k_h,
@@ -285,7 +378,8 @@ int pxa_sparse_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const 
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {row_ptr, 4}, {col_idx, 4}, {o, 16}}))) return rc;
   if (row_order && !aligned(row_order, 4)) return PXA_EALIGN;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg, opts), q, k, v, row_ptr, col_idx, row_order,
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  return hip_rc(pxa::launch_fa_prefill(a, pxa::one_seq(a), q, k, v, row_ptr, col_idx, row_order,
                                        o, false, (hipStream_t)stream));
 }
 
@@ -300,7 +394,8 @@ int pxa_dense_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const v
   int rc = check_all(cfg, opts);
   if (rc) return rc;
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}}))) return rc;
-  return hip_rc(pxa::launch_fa_prefill(args_of(cfg, opts), q, k, v, nullptr, nullptr, nullptr, o,
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  return hip_rc(pxa::launch_fa_prefill(a, pxa::one_seq(a), q, k, v, nullptr, nullptr, nullptr, o,
                                        true, (hipStream_t)stream));
 }
 
@@ -319,28 +414,7 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* budget, const void*
   layout_of(cfg, budget, &L);
   if (ws_bytes < L.total) return PXA_EWORKSPACE;
   const pxa::LaunchArgs a = args_of(cfg, budget);
-  hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  void* qbar = w + L.qbar;
-  void* kbar = w + L.kbar;
-  float* scores = (float*)(w + L.scores);
-  float* masses = (float*)(w + L.masses);
-  int32_t* k_h = (int32_t*)(w + L.k_h);
-  int32_t* row_ptr = (int32_t*)(w + L.row_ptr);
-  int32_t* col_idx = (int32_t*)(w + L.col_idx);
-  int32_t* row_order = (int32_t*)(w + L.row_order);
-  if ((rc = hip_rc(pxa::launch_proxy_pool(a, q, k, qbar, kbar, s)))) return rc;
-  if ((rc = hip_rc(pxa::launch_proxy_score(a, qbar, kbar, scores, s)))) return rc;
-  if (a.budget_mode == pxa::kBudgetDynamic)
-    rc = hip_rc(pxa::launch_budget(a, q, k, scores, k_h, masses, w + L.budget_ws, s));
-  else if (a.budget_mode == pxa::kBudgetFixed)
-    rc = hip_rc(pxa::launch_fixed_budget(a, k_h, s));
-  if (rc) return rc;
-  const bool ratio = a.budget_mode == pxa::kBudgetRatio;
-  if ((rc = hip_rc(pxa::launch_select(a, scores, ratio ? nullptr : k_h, row_ptr, col_idx,
-                                      row_order, w + L.select_ws, s))))
-    return rc;
-  return hip_rc(pxa::launch_fa_prefill(a, q, k, v, row_ptr, col_idx, row_order, o, false, s));
+  return run_method(a, pxa::one_seq(a), q, k, v, o, ws, L, (hipStream_t)stream);
 }
 
 int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
@@ -348,33 +422,63 @@ int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void*
   return pxa_prefill_ex(cfg, nullptr, q, k, v, o, ws, ws_bytes, stream);
 }
 
+size_t pxa_batch_workspace_bytes(const pxa_config* cfg, const pxa_options* opts,
+                                 int32_t num_seqs, const int32_t* seq_lens) {
+  if (check_all(cfg, opts) != PXA_OK) return 0;
+  if (check_lengths(cfg, opts, num_seqs, seq_lens) != PXA_OK) return 0;
+  return fused_bytes(cfg, opts, num_seqs, seq_lens);
+}
+
+int pxa_get_batch_workspace_layout(const pxa_config* cfg, const pxa_options* opts,
+                                   int32_t num_seqs, const int32_t* seq_lens,
+                                   pxa_workspace_layout* out) {
+  int rc = check_all(cfg, opts);
+  if (rc) return rc;
+  if ((rc = check_lengths(cfg, opts, num_seqs, seq_lens))) return rc;
+  if (!out) return PXA_ENULL;
+  int groups = 0;
+  for_each_group(cfg, num_seqs, seq_lens, [&](int32_t, int32_t) { ++groups; });
+  if (groups != 1) return PXA_EINVAL;   // more than one fused group
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  layout_of_table(a, pxa::make_table(seq_lens, num_seqs, a.G, a.score_stride), out);
+  return PXA_OK;
+}
+
 int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t num_seqs,
                       const int32_t* seq_lens, const void* q, const void* k, const void* v,
                       void* o, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_all(cfg, opts);
   if (rc) return rc;
-  if (num_seqs < 1) return PXA_EINVAL;
-  if (!seq_lens) return PXA_ENULL;
+  if ((rc = check_lengths(cfg, opts, num_seqs, seq_lens))) return rc;   // before any launch
   if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}, {ws, 256}}))) return rc;
-  if (ws_bytes < pxa_workspace_bytes_ex(cfg, opts)) return PXA_EWORKSPACE;
-  for (int32_t s = 0; s < num_seqs; ++s) {   // validate every length before any launch
-    const int32_t n = seq_lens[s];
-    if (n < 1 || n > cfg->seq_len) return PXA_EINVAL;
-    pxa_config c = *cfg;
-    c.seq_len = n;
-    if ((rc = check_all(&c, opts))) return rc;   // e.g. a probe longer than this sequence
-  }
+  const pxa::LaunchArgs a = args_of(cfg, opts);
   const size_t qrow = (size_t)cfg->num_heads * cfg->head_dim * 2;      // bytes per token
   const size_t krow = (size_t)cfg->num_kv_heads * cfg->head_dim * 2;
-  size_t qoff = 0, koff = 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (ws_bytes >= fused_bytes(cfg, opts, num_seqs, seq_lens)) {
+    // fused: one set of launches per group of sequences
+    size_t tok = 0;
+    for_each_group(cfg, num_seqs, seq_lens, [&](int32_t first, int32_t cnt) {
+      if (rc) return;
+      const pxa::SeqTable t = pxa::make_table(seq_lens + first, cnt, a.G, a.score_stride);
+      pxa_workspace_layout L;
+      layout_of_table(a, t, &L);
+      rc = run_method(a, t, (const char*)q + qrow * tok, (const char*)k + krow * tok,
+                      (const char*)v + krow * tok, (char*)o + qrow * tok, ws, L, st);
+      tok += (size_t)t.tok[t.n];
+    });
+    return rc;
+  }
+  // sequence by sequence in a workspace sized for the longest one
+  if (ws_bytes < pxa_workspace_bytes_ex(cfg, opts)) return PXA_EWORKSPACE;
+  size_t tok = 0;
   for (int32_t s = 0; s < num_seqs; ++s) {
     pxa_config c = *cfg;
     c.seq_len = seq_lens[s];
-    rc = pxa_prefill_ex(&c, opts, (const char*)q + qoff, (const char*)k + koff,
-                        (const char*)v + koff, (char*)o + qoff, ws, ws_bytes, stream);
+    rc = pxa_prefill_ex(&c, opts, (const char*)q + qrow * tok, (const char*)k + krow * tok,
+                        (const char*)v + krow * tok, (char*)o + qrow * tok, ws, ws_bytes, stream);
     if (rc) return rc;
-    qoff += qrow * (size_t)c.seq_len;
-    koff += krow * (size_t)c.seq_len;
+    tok += (size_t)c.seq_len;
   }
   return PXA_OK;
 }

@@ -238,6 +238,20 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sequence of a fused launch that holds item x: the s with pre[s] <= x <
+// pre[s+1] (pre: one of the SeqTable prefix arrays, x < pre[n]).  Binary
+// search on wave-uniform values, so it runs on scalar loads of the kernel
+// arguments.
+__device__ __forceinline__ int seq_find(const int32_t* pre, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
 // Order-preserving map of a finite float to uint32 (larger float -> larger
 // code); -0 is folded onto +0 first so that equal scores compare equal.
 __device__ __forceinline__ uint32_t float_order_key(float f) {

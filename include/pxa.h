@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 6
+#define PXA_ABI_VERSION 7
 
 enum {
   PXA_OK = 0,
@@ -161,17 +161,40 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q
                    const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                    void* stream);
 
-/* Several sequences in one call (batched prefill, equal or different
- * lengths).  Sequence s has seq_lens[s] tokens (host array; each in
- * [1, cfg->seq_len], cfg->seq_len sizing the workspace); its tensors are
- * the usual per-sequence blocks Q/O [H][N_s][d], K/V [Hkv][N_s][d], stored one
- * after another (sequence s starts after the elements of sequences 0..s-1).
- * The whole method runs on each sequence in order on `stream` with the same
- * workspace (pxa_workspace_bytes_ex(cfg, opts)); the workspace keeps the
- * intermediates of the last sequence.  Each sequence's output equals what
- * pxa_prefill_ex gives for it alone.  PXA_EINVAL for num_seqs < 1, a length
- * outside [1, cfg->seq_len] or a probe longer than a sequence, PXA_ENULL for a
- * NULL seq_lens.  Every length is checked before the first launch. */
+/* Several sequences in one call (batched / packed varlen prefill, equal or
+ * different lengths).  Sequence s has seq_lens[s] tokens (host array; each in
+ * [1, cfg->seq_len]); its tensors are the usual per-sequence blocks
+ * Q/O [H][N_s][d], K/V [Hkv][N_s][d], stored one after another (sequence s
+ * starts after the elements of sequences 0..s-1).  Each sequence's output
+ * equals what pxa_prefill_ex gives for it alone.
+ *   Fused (ws_bytes >= pxa_batch_workspace_bytes): the sequences are taken in
+ * groups of up to PXA_MAX_FUSED_SEQS consecutive ones and each group runs as
+ * one set of launches (one grid per stage over every block of every sequence
+ * of the group, one CSR and one attention schedule for the whole group), so
+ * many short sequences fill the GPU together.  The workspace then holds the
+ * last group's intermediates, laid out as pxa_get_batch_workspace_layout
+ * gives for that group.
+ *   Otherwise (ws_bytes >= pxa_workspace_bytes_ex(cfg, opts), cfg->seq_len
+ * the longest length): one sequence at a time, the workspace holding the last
+ * sequence's intermediates.
+ * PXA_EINVAL for num_seqs < 1, a length outside [1, cfg->seq_len] or a probe
+ * longer than a sequence, PXA_ENULL for a NULL seq_lens, PXA_EWORKSPACE below
+ * both sizes.  Every length is checked before the first launch. */
+#define PXA_MAX_FUSED_SEQS 64
+/* Workspace bytes for the fused batch path: the largest group's; 0 if
+ * cfg, opts or the lengths are invalid. */
+size_t pxa_batch_workspace_bytes(const pxa_config* cfg, const pxa_options* opts,
+                                 int32_t num_seqs, const int32_t* seq_lens);
+/* Layout of the fused workspace of a batch that forms one group (at most
+ * PXA_MAX_FUSED_SEQS sequences): every part is the concatenation of the
+ * sequences' own parts in order (qbar/kbar [G][N_s][d] each, scores
+ * [G][nb_s][nb_s] each, masses [H][nb_s] each, k_h [H] each, then one CSR
+ * over all rows -- sequence s's H*nb_s rows after those of the sequences
+ * before it, column indices local to the sequence -- and one row_order over
+ * those rows).  PXA_EINVAL if the batch forms more than one group. */
+int pxa_get_batch_workspace_layout(const pxa_config* cfg, const pxa_options* opts,
+                                   int32_t num_seqs, const int32_t* seq_lens,
+                                   pxa_workspace_layout* out);
 int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t num_seqs,
                       const int32_t* seq_lens, const void* q, const void* k, const void* v,
                       void* o, void* ws, size_t ws_bytes, void* stream);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 6
+    assert pxa.pxa_abi_version() == 7
 
 
 def test_struct_layouts_match_header():
@@ -135,8 +135,10 @@ def test_batch_entry_point_validates_before_launch():
             A, A, A, A, A, ws_bytes=1 << 40, stream=0)   # 100 tokens: one (partial) block < 2
     _expect(B.PXA_EINVAL, pxa.pxa_prefill_batch, cfg, pxa.Options.dynamic(4), [1024, 256],
             A, A, A, A, A, ws_bytes=1 << 40, stream=0)   # probe of 4 blocks > 2 blocks
+    fused = pxa.pxa_batch_workspace_bytes(cfg, None, [256])
+    assert 0 < fused < big
     _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_batch, cfg, None, [256], A, A, A, A, A,
-            ws_bytes=big - 256, stream=0)
+            ws_bytes=fused - 256, stream=0)          # below the fused and the per-sequence size
     _expect(B.PXA_EALIGN, pxa.pxa_prefill_batch, cfg, None, [256], MIS, A, A, A, A,
             ws_bytes=big, stream=0)
     lib = pxa.load_library()
@@ -309,3 +311,69 @@ def test_partial_last_block_sizes():
     assert pxa.pxa_validate_options(cfg, pxa.Options.dynamic(9)) == B.PXA_EINVAL
     one = _good(seq_len=5)
     assert one.nb == 1 and pxa.pxa_max_col_entries(one) == H
+
+
+def _layout_sizes(H, G, d, lens, m=1):
+    """Byte sizes of the fused workspace parts, summed over the sequences."""
+    nbs = [-(-n // 128) for n in lens]
+    toks, blks = sum(lens), sum(nbs)
+    return {"qbar": G * toks * d * 2, "kbar": G * toks * d * 2,
+            "scores": G * sum(nb * nb for nb in nbs) * 4, "masses": H * blks * 4,
+            "k_h": H * len(lens) * 4, "row_ptr": (H * blks + 1) * 4,
+            "col_idx": H * sum(nb * (nb + 1) // 2 for nb in nbs) * 4,
+            "row_order": H * blks * 4, "budget_ws": H * m * blks * 128 * 4,
+            "select_ws": 2 * H * blks * 4}
+
+
+def test_batch_workspace_of_one_sequence_is_the_single_workspace():
+    for n in (1024, 1000, 5):
+        cfg = _good(seq_len=n)
+        for opts in (None, pxa.Options.dynamic(1), pxa.Options.ratio_of(0.2, score_stride=4)):
+            assert pxa.pxa_batch_workspace_bytes(cfg, opts, [n]) == pxa.pxa_workspace_bytes_ex(cfg, opts)
+            a, b = pxa.pxa_get_batch_workspace_layout(cfg, opts, [n]), pxa.pxa_get_workspace_layout_ex(cfg, opts)
+            for f, _ in B.pxa_workspace_layout._fields_:
+                assert getattr(a, f) == getattr(b, f), f
+
+
+def test_batch_workspace_layout_concatenates_the_sequences():
+    lens = [300, 1000, 77, 1024]
+    cfg = _good()                                   # H 8, G 2, d 128, seq_len 1024
+    L = pxa.pxa_get_batch_workspace_layout(cfg, None, lens)
+    sizes = _layout_sizes(8, 2, 128, lens)
+    order = ["qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx", "row_order",
+             "budget_ws", "select_ws"]
+    prev_end = 0
+    for name in order:
+        off = getattr(L, name)
+        assert off % 256 == 0 and off >= prev_end, name
+        prev_end = off + sizes[name]
+    assert L.total >= prev_end and L.total == pxa.pxa_batch_workspace_bytes(cfg, None, lens)
+    # a probe of 2 blocks doubles the budget scratch; the 77-token sequence has one block
+    assert pxa.pxa_batch_workspace_bytes(cfg, pxa.Options.dynamic(2), lens) == 0
+    assert pxa.pxa_batch_workspace_bytes(cfg, pxa.Options.dynamic(2), [300, 1000]) > \
+        pxa.pxa_batch_workspace_bytes(cfg, None, [300, 1000])
+
+
+def test_batch_groups_of_at_most_64_sequences():
+    cfg = _good()
+    assert B.PXA_MAX_FUSED_SEQS == 64
+    one = pxa.pxa_batch_workspace_bytes(cfg, None, [128] * 64)
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [128] * 65) == one       # groups 64 + 1
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [128] * 128) == one      # 64 + 64
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [128] * 64 + [1024]) == one   # 64-group larger
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [128] * 63 + [1024]) > one    # one group
+    pxa.pxa_get_batch_workspace_layout(cfg, None, [128] * 64)
+    _expect(B.PXA_EINVAL, pxa.pxa_get_batch_workspace_layout, cfg, None, [128] * 65)
+
+
+def test_batch_workspace_invalid_inputs():
+    cfg = _good()
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, []) == 0
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [0]) == 0
+    assert pxa.pxa_batch_workspace_bytes(cfg, None, [2048]) == 0        # above cfg.seq_len
+    assert pxa.pxa_batch_workspace_bytes(_good(head_dim=96), None, [128]) == 0
+    _expect(B.PXA_EINVAL, pxa.pxa_get_batch_workspace_layout, cfg, None, [])
+    # below both the fused and the one-at-a-time size
+    least = min(pxa.pxa_workspace_bytes(cfg), pxa.pxa_batch_workspace_bytes(cfg, None, [256, 256]))
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_batch, cfg, None, [256, 256], A, A, A, A, A,
+            ws_bytes=least - 256, stream=0)

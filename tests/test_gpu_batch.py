@@ -9,7 +9,8 @@ torch = pytest.importorskip("torch")
 import block_sparse_long_proxy_amd as pxa  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from synth import CONFIGS, generate, bf16_bits_to_f32, to_bf16_bits  # noqa: E402
-from parity_util import gpu_bf16, csr_to_keep, compare_masks, assert_outputs_close, MASK_AGREE  # noqa: E402
+from parity_util import (  # noqa: E402
+    gpu_bf16, csr_to_keep, compare_masks, assert_outputs_close, check_schedule, MASK_AGREE)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,15 +23,25 @@ def _seqs():
     return [generate(base.with_(name=f"seq{i}", seq_len=n, seed=40 + i)) for i, n in enumerate(LENS)]
 
 
+def _ws_bytes(path, cfg, opts, lens):
+    fused = pxa.pxa_batch_workspace_bytes(cfg, opts, lens)
+    single = pxa.pxa_workspace_bytes_ex(cfg, opts)
+    if path == "fused":
+        return fused
+    assert single < fused          # so the call takes the one-sequence-at-a-time path
+    return single
+
+
+@pytest.mark.parametrize("path", ["fused", "sequential"])
 @pytest.mark.parametrize("opts", [None, pxa.Options.ratio_of(0.3, score_stride=2)],
                          ids=["default", "ratio_stride2"])
-def test_batch_equals_one_call_per_sequence(opts):
+def test_batch_equals_one_call_per_sequence(opts, path):
     xs = _seqs()
     H, Hkv, d = 8, 2, 128
     cfg = pxa.Config(H, Hkv, max(LENS), d, 2, 0.9)
     flat = {n: torch.cat([gpu_bf16(x[n]).reshape(-1) for x in xs]) for n in ("q", "k", "v")}
     o = torch.full_like(flat["q"], float("nan"))
-    ws = torch.empty(pxa.pxa_workspace_bytes_ex(cfg, opts), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(_ws_bytes(path, cfg, opts, LENS), dtype=torch.uint8, device="cuda")
     pxa.pxa_prefill_batch(cfg, opts, LENS, flat["q"], flat["k"], flat["v"], o, ws)
     torch.cuda.synchronize()
     off = 0
@@ -71,3 +82,48 @@ def test_batch_sequence_against_oracle():
     assert frac >= MASK_AGREE and not rep["bad"]
     got = o[-H * n * d:].view(H, n, d).float().cpu().numpy().astype(np.float64)
     assert_outputs_close(got, O.sparse_attention(q, k, v, keep, 128, c.scale), "last sequence")
+
+
+def _i32(ws, off, n):
+    return ws[off:off + 4 * n].view(torch.int32)
+
+
+def _f32(ws, off, n):
+    return ws[off:off + 4 * n].view(torch.float32)
+
+
+def test_fused_batch_intermediates_are_each_sequences_own():
+    """The fused workspace holds, part by part, every sequence's intermediates
+    as a call for that sequence alone writes them (rows of the shared CSR
+    shifted by the rows before the sequence)."""
+    xs = _seqs()
+    H, Hkv, d, G = 8, 2, 128, 2
+    cfg = pxa.Config(H, Hkv, max(LENS), d, G, 0.9)
+    flat = {n: torch.cat([gpu_bf16(x[n]).reshape(-1) for x in xs]) for n in ("q", "k", "v")}
+    o = torch.empty_like(flat["q"])
+    L = pxa.pxa_get_batch_workspace_layout(cfg, None, LENS)
+    ws = torch.empty(L.total, dtype=torch.uint8, device="cuda")
+    pxa.pxa_prefill_batch(cfg, None, LENS, flat["q"], flat["k"], flat["v"], o, ws)
+    torch.cuda.synchronize()
+    nbs = [n // 128 for n in LENS]
+    blk = sq = 0
+    rows_before = 0
+    for s_, (x, n, nb) in enumerate(zip(xs, LENS, nbs)):
+        attn = pxa.ProxyAttn(pxa.Config(H, Hkv, n, d, G, 0.9))
+        attn(gpu_bf16(x["q"]), gpu_bf16(x["k"]), gpu_bf16(x["v"]))
+        torch.cuda.synchronize()
+        assert torch.equal(_f32(ws, L.scores + 4 * G * sq, G * nb * nb), attn.scores.reshape(-1))
+        assert torch.equal(_f32(ws, L.masses + 4 * H * blk, H * nb), attn.masses.reshape(-1))
+        assert torch.equal(_i32(ws, L.k_h + 4 * H * s_, H), attn.k_h)
+        rp = _i32(ws, L.row_ptr + 4 * H * blk, H * nb + 1).cpu().numpy().astype(np.int64)
+        rp1 = attn.row_ptr.cpu().numpy().astype(np.int64)
+        np.testing.assert_array_equal(rp - rp[0], rp1)
+        ci = _i32(ws, L.col_idx + 4 * int(rp[0]), int(rp1[-1]))
+        assert torch.equal(ci, attn.col_idx[: int(rp1[-1])])
+        blk += nb
+        sq += nb * nb
+        rows_before += H * nb
+    # one schedule over all rows of the batch
+    order = _i32(ws, L.row_order, H * blk).cpu().numpy()
+    full_rp = _i32(ws, L.row_ptr, H * blk + 1).cpu().numpy()
+    check_schedule(order, full_rp)

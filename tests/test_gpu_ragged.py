@@ -298,7 +298,8 @@ def test_ragged_skip_parity(name, lam):
     assert checked >= H
 
 
-def test_ragged_batch_equals_one_call_per_sequence():
+@pytest.mark.parametrize("path", ["fused", "sequential"])
+def test_ragged_batch_equals_one_call_per_sequence(path):
     lens = [300, 1000, 77, 128, 1]
     H, Hkv, d = 8, 2, 128
     base = BASE.with_(num_heads=H, num_kv_heads=Hkv, head_dim=d, num_proxies=2, gammas=(0.9,),
@@ -309,7 +310,9 @@ def test_ragged_batch_equals_one_call_per_sequence():
     opts = Options.dynamic(score_stride=2)
     flat = {n: torch.cat([gpu_bf16(x[n]).reshape(-1) for x in xs]) for n in ("q", "k", "v")}
     o = torch.full_like(flat["q"], float("nan"))
-    ws = torch.empty(pxa.pxa_workspace_bytes_ex(cfg, opts), dtype=torch.uint8, device="cuda")
+    fused, single = pxa.pxa_batch_workspace_bytes(cfg, opts, lens), pxa.pxa_workspace_bytes_ex(cfg, opts)
+    assert single < fused
+    ws = torch.empty(fused if path == "fused" else single, dtype=torch.uint8, device="cuda")
     pxa.pxa_prefill_batch(cfg, opts, lens, flat["q"], flat["k"], flat["v"], o, ws)
     torch.cuda.synchronize()
     off = 0
@@ -320,3 +323,31 @@ def test_ragged_batch_equals_one_call_per_sequence():
         assert torch.equal(o[off:off + H * n * d].view(H, n, d), ref), f"sequence of {n} tokens"
         off += H * n * d
     assert off == o.numel()
+
+
+def test_fused_batch_of_seventy_short_sequences():
+    """70 sequences (two fused groups: 64 + 6) of 1..700 tokens: each output
+    equals a call for that sequence alone, and nothing is written past the end."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 700, size=70)]
+    H, Hkv, d = 4, 2, 64
+    base = BASE.with_(num_heads=H, num_kv_heads=Hkv, head_dim=d, num_proxies=2, gammas=(0.9,))
+    xs = [generate(base.with_(name=f"s{i}", seq_len=n, seed=200 + i, n_needles=min(n, 4)))
+          for i, n in enumerate(lens)]
+    cfg = pxa.Config(H, Hkv, max(lens), d, 2, 0.9)
+    flat = {n: torch.cat([gpu_bf16(x[n]).reshape(-1) for x in xs]) for n in ("q", "k", "v")}
+    total = flat["q"].numel()
+    buf = torch.full((total + 128 * d,), 7.0, dtype=torch.bfloat16, device="cuda")
+    o = buf[:total]
+    ws = torch.empty(pxa.pxa_batch_workspace_bytes(cfg, None, lens), dtype=torch.uint8, device="cuda")
+    pxa.pxa_prefill_batch(cfg, None, lens, flat["q"], flat["k"], flat["v"], o, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.all(buf[total:] == 7.0))
+    off = 0
+    for x, n in zip(xs, lens):
+        attn = pxa.ProxyAttn(pxa.Config(H, Hkv, n, d, 2, 0.9))
+        ref = attn(gpu_bf16(x["q"]), gpu_bf16(x["k"]), gpu_bf16(x["v"]))
+        torch.cuda.synchronize()
+        assert torch.equal(o[off:off + H * n * d].view(H, n, d), ref), f"sequence of {n} tokens"
+        off += H * n * d
+    assert off == total
