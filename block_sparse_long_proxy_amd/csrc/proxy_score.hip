@@ -15,8 +15,10 @@
 // workgroup serves s consecutive rows, 128/s queries each, so the per-tile
 // work and the reuse of each K tile stay those of s = 1.
 //
-// One workgroup of four waves per proxy g and query-block row I, two
-// workgroups per CU (they run out of phase, so one's maxima and barriers
+// One workgroup of four waves per proxy g and query-block row I (or, when
+// few long rows would leave the chip idle, per 64-tile multiple of a row's
+// key range: the chunks write disjoint score entries, so nothing is merged),
+// two workgroups per CU (they run out of phase, so one's maxima and barriers
 // overlap the other's MFMAs).  Key tiles J = 0..I stream through a two-deep
 // LDS ring filled by direct global->LDS copies (tile J+1 lands while J is
 // used).  Each wave computes 32 keys of the tile against all 128 proxy queries
@@ -26,6 +28,8 @@
 // wave with DPP moves (no LDS round trips), and kept in lane J mod 64; every
 // 64 tiles the four waves combine their maxima through LDS and store them as
 // one coalesced run, so the only per-tile barrier is the one guarding the ring.
+#include <type_traits>
+
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -35,10 +39,12 @@ constexpr int kScoreBufs = 2;                  // K tile in use + the next one i
 
 // STRIDE s: the block's queries at offsets s-1, 2s-1, ..., 127 are scored
 // (128/s of them, in QC = 4/s chunks of 32); s = 1 scores every query.
-template <int D, int STRIDE>
+// SPLIT: workgroups cover W-tile parts of the rows (template parameter so the
+// whole-row launches carry none of that index arithmetic).
+template <int D, int STRIDE, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
-    int G, float scale, const SeqTable t) {
+    int G, float scale, int W, const SeqTable t) {
   // STRIDE s: rows I0, I0-1, ..., I0-s+1 share the workgroup, each with its
   // 128/s scored queries (offsets s-1, 2s-1, ..., 127), so every wave still
   // holds 4 chunks of 32 queries and each K tile feeds the same MFMA work.
@@ -51,15 +57,29 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   // sequence of a fused batch (its workgroups are consecutive), then this
   // sequence's proxies and score grid
   const int sid = t.n == 1 ? 0 : seq_find(t.swg, t.n, (int)blockIdx.x);
-  const int bl = (int)blockIdx.x - t.swg[sid];
+  int bl = (int)blockIdx.x - t.swg[sid];
   const int N = t.tok[sid + 1] - t.tok[sid];
   qbar += (size_t)t.tok[sid] * G * D;
   kbar += (size_t)t.tok[sid] * G * D;
   scores += (size_t)G * t.sq[sid];
   const int nb = t.blk[sid + 1] - t.blk[sid];
   const int tail = N - (nb - 1) * kBlock;        // tokens of the last block (128 unless partial)
+  // Level lev of a row group covers its key tiles [lev W, lev W + W); the
+  // row groups that reach level lev are the ceil((nb - lev W) / R) longest
+  // ones.  W >= nb: one level, a workgroup per row group.
+  int lev = 0;
+  if (SPLIT) {
+    for (;;) {
+      const int n_lev = G * ((nb - lev * W + R - 1) / R);
+      if (bl < n_lev) break;
+      bl -= n_lev;
+      ++lev;
+    }
+  }
   const int g = bl % G;
   const int I0 = nb - 1 - R * (bl / G);          // top row; longest rows first
+  const int J0 = SPLIT ? lev * W : 0;            // this workgroup's key tiles J0 .. J1
+  const int J1 = SPLIT ? min(I0, J0 + W - 1) : I0;
   const int ws = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));   // keys 32 ws ..
   const int l = threadIdx.x & 63;
   const int hi = l >> 5;
@@ -83,12 +103,14 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     }
   }
   const __bf16* kb = uniform_ptr(kbar + (size_t)g * N * D);
+  if (lev == 0) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int Ir = I0 - r;
-    if (Ir < 0) continue;
-    float* srow = scores + ((size_t)g * nb + Ir) * nb;
-    for (int J = Ir + 1 + threadIdx.x; J < nb; J += kThreads) srow[J] = -INFINITY;
+    for (int r = 0; r < R; ++r) {
+      const int Ir = I0 - r;
+      if (Ir < 0) continue;
+      float* srow = scores + ((size_t)g * nb + Ir) * nb;
+      for (int J = Ir + 1 + threadIdx.x; J < nb; J += kThreads) srow[J] = -INFINITY;
+    }
   }
   // Threads 0..64R-1: combine chunk cc (tiles 64cc .. 64cc+63) of the four
   // key slices, for row I0 - (thread / 64).
@@ -112,15 +134,15 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     else
       tile_load_lds<D, false>(kb + (size_t)J * kTile, buf);
   };
-  load_tile(0, kt[0]);
+  load_tile(J0, kt[J0 % kScoreBufs]);
   float keep[R];                                 // this wave's max of tile J per row, lane J mod 64
 #pragma unroll
   for (int r = 0; r < R; ++r) keep[r] = -INFINITY;
-  for (int J = 0; J <= I0; ++J) {
+  for (int J = J0; J <= J1; ++J) {
     wait_vmem();       // this thread's part of tile J (the only copy in flight)
     __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
-    if (J + 1 <= I0) load_tile(J + 1, kt[(J + 1) % kScoreBufs]);
-    if (J > 0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
+    if (J + 1 <= J1) load_tile(J + 1, kt[(J + 1) % kScoreBufs]);
+    if (J > J0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
     const __bf16* cur = kt[J % kScoreBufs];
     f32x16 acc[4];
 #pragma unroll
@@ -160,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       mx = wave_max_uniform(mx);
       if (l == (J & 63)) keep[r] = mx;
     }
-    if ((J & 63) == 63 || J == I0) {
+    if ((J & 63) == 63 || J == J1) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         wm[(J >> 6) & 1][r][ws][l] = keep[r];
@@ -168,26 +190,59 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       }
     }
   }
+  // J1 ends a 64-tile chunk or is I0, so every entry stored was computed here
   __syncthreads();
-  store_chunk(I0 >> 6);
+  store_chunk(J1 >> 6);
 }
+
+// Workgroup slots of the chip for this kernel (256 CUs, two workgroups each).
+constexpr long kScoreSlots = 512;
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const SeqTable& t, const void* qbar,
                               const void* kbar, float* scores, hipStream_t stream) {
-  const dim3 grid(t.swg[t.n]), block(kThreads);
+  // Key tiles per workgroup: whole rows when the longest row is at most half
+  // the mean load of a slot (the longest-first order then balances), else
+  // multiples of 64 tiles near that half, so a few long rows do not leave
+  // most of the chip idle.
+  const int R = a.score_stride;
+  long tiles = 0;
+  int nbmax = 0;
+  for (int s = 0; s < t.n; ++s) {
+    const int nb = t.blk[s + 1] - t.blk[s];
+    nbmax = nb > nbmax ? nb : nbmax;
+    for (int top = nb; top > 0; top -= R) tiles += (long)a.G * top;   // row group: top tiles
+  }
+  const long half_mean = tiles / kScoreSlots / 2;
+  int W = (int)align_up((size_t)nbmax, 64);
+  if (nbmax > half_mean) W = (int)(half_mean / 64 > 1 ? half_mean / 64 * 64 : 64);
+  SeqTable tw = t;   // workgroup prefix for this chunking
+  tw.swg[0] = 0;
+  for (int s = 0; s < t.n; ++s) {
+    const int nb = t.blk[s + 1] - t.blk[s];
+    int wgs = 0;
+    for (int lev = 0; nb - lev * W > 0; ++lev) wgs += a.G * ((nb - lev * W + R - 1) / R);
+    tw.swg[s + 1] = tw.swg[s] + wgs;
+  }
+  const dim3 grid(tw.swg[t.n]), block(kThreads);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)qbar, (const __bf16*)kbar,
-                       scores, a.G, a.scale, t);
+                       scores, a.G, a.scale, W, tw);
   };
-  if (a.D == 64) {
-    if (a.score_stride == 4) go(proxy_score_kernel<64, 4>);
-    else if (a.score_stride == 2) go(proxy_score_kernel<64, 2>);
-    else go(proxy_score_kernel<64, 1>);
-  } else {
-    if (a.score_stride == 4) go(proxy_score_kernel<128, 4>);
-    else if (a.score_stride == 2) go(proxy_score_kernel<128, 2>);
-    else go(proxy_score_kernel<128, 1>);
-  }
+  const bool split = W < nbmax;
+  auto pick = [&](auto d) {
+    constexpr int D = decltype(d)::value;
+    if (split) {
+      if (a.score_stride == 4) go(proxy_score_kernel<D, 4, true>);
+      else if (a.score_stride == 2) go(proxy_score_kernel<D, 2, true>);
+      else go(proxy_score_kernel<D, 1, true>);
+    } else {
+      if (a.score_stride == 4) go(proxy_score_kernel<D, 4, false>);
+      else if (a.score_stride == 2) go(proxy_score_kernel<D, 2, false>);
+      else go(proxy_score_kernel<D, 1, false>);
+    }
+  };
+  if (a.D == 64) pick(std::integral_constant<int, 64>{});
+  else pick(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 

@@ -351,3 +351,27 @@ def test_fused_batch_of_seventy_short_sequences():
         assert torch.equal(o[off:off + H * n * d].view(H, n, d), ref), f"sequence of {n} tokens"
         off += H * n * d
     assert off == total
+
+
+@pytest.mark.parametrize("stride", [1, 2, 4])
+def test_split_score_rows_of_a_long_sequence(stride):
+    """40,000 tokens with one proxy: few rows for the chip, so the score kernel
+    splits each row's key range into 64-tile parts (the last block holds 64
+    tokens).  Sampled rows around the part boundaries against the oracle on
+    identical proxies; every causal entry finite, every other -inf."""
+    N, d = 40000, 64
+    wl = BASE.with_(name="n40000", num_heads=4, num_kv_heads=2, head_dim=d, seq_len=N,
+                    num_proxies=1, seed=31, n_needles=16)
+    x = generate(wl)
+    cfg = pxa.Config(4, 2, N, d, 1, wl.gamma)
+    nb = cfg.nb
+    dev = {n: gpu_bf16(x[n]) for n in ("q", "k")}
+    qb, kb = _pool(cfg, dev)
+    S = host64(_score(cfg, qb, kb, Options.dynamic(score_stride=stride)))
+    tri = np.tril(np.ones((nb, nb), dtype=bool))
+    assert np.all(np.isfinite(S[0][tri])) and np.all(np.isneginf(S[0][~tri]))
+    qh, kh = host64(qb)[0], host64(kb)[0]
+    for I in (0, 62, 63, 64, 65, 127, 128, 191, 250, nb - 2, nb - 1):
+        ref = O.proxy_score_row(qh, kh, I, 128, cfg.scale, stride)
+        err = np.abs(S[0, I, : I + 1] - ref)
+        assert np.all(err <= SCORE_RTOL * np.maximum(np.abs(ref), 1.0)), (I, float(err.max()))
