@@ -33,8 +33,10 @@ def _ws_bytes(path, cfg, opts, lens):
 
 
 @pytest.mark.parametrize("path", ["fused", "sequential"])
-@pytest.mark.parametrize("opts", [None, pxa.Options.ratio_of(0.3, score_stride=2)],
-                         ids=["default", "ratio_stride2"])
+@pytest.mark.parametrize("opts", [None, pxa.Options.ratio_of(0.3, score_stride=2),
+                                  pxa.Options.fixed(3, score_stride=4),
+                                  pxa.Options.dynamic(skip_threshold=0.05)],
+                         ids=["default", "ratio_stride2", "fixed3_stride4", "skip"])
 def test_batch_equals_one_call_per_sequence(opts, path):
     xs = _seqs()
     H, Hkv, d = 8, 2, 128
