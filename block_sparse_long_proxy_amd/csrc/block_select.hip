@@ -90,6 +90,59 @@ __device__ __forceinline__ int xcd_of_row(int64_t start, int len, int64_t total)
   return (int)min<int64_t>(x, kXcds - 1);
 }
 
+// f(i, counts[i]) for i in [a, b) in order, the loads issued eight at a time
+// (one at a time, these loops wait out a memory latency per row).
+template <typename F>
+__device__ __forceinline__ void for_counts(const int32_t* __restrict__ counts, int a, int b,
+                                           F&& f) {
+  int i = a;
+  for (; i + 8 <= b; i += 8) {
+    int c[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c[u] = counts[i + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f(i + u, c[u]);
+  }
+  for (; i < b; ++i) f(i, counts[i]);
+}
+
+// f(r, counts[r], row_ptr[r]) for the rows r = tmp[p], p in [a, b), in order,
+// with the loads batched the same way.
+template <typename F>
+__device__ __forceinline__ void for_order(const int32_t* __restrict__ tmp,
+                                          const int32_t* __restrict__ counts,
+                                          const int32_t* __restrict__ row_ptr, int a, int b,
+                                          F&& f) {
+  int p = a;
+  for (; p + 8 <= b; p += 8) {
+    int r[8], c[8], s[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) r[u] = tmp[p + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c[u] = counts[r[u]];
+      s[u] = row_ptr[r[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) f(r[u], c[u], s[u]);
+  }
+  for (; p < b; ++p) {
+    const int r = tmp[p];
+    f(r, counts[r], row_ptr[r]);
+  }
+}
+
+// Inclusive Hillis-Steele scan of part[0..kScanThreads) in place.
+__device__ __forceinline__ void block_scan(int* part) {
+  const int t = threadIdx.x;
+  for (int off = 1; off < kScanThreads; off <<= 1) {
+    const int x = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += x;
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t* __restrict__ counts,
                                                                    int32_t* __restrict__ row_ptr,
                                                                    int32_t* __restrict__ row_order,
@@ -103,49 +156,50 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
   const int per = (n + kScanThreads - 1) / kScanThreads;
   const int a = min(n, t * per), b = min(n, a + per);
   int s = 0;
-  for (int i = a; i < b; ++i) s += counts[i];
+  for_counts(counts, a, b, [&](int, int c) { s += c; });
   part[t] = s;
   if (row_order)
     for (int c = t; c <= max_len; c += kScanThreads) hist[c] = 0;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive Hillis-Steele
-    const int x = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
+  block_scan(part);
   int run = part[t] - s;
-  for (int i = a; i < b; ++i) {
+  for_counts(counts, a, b, [&](int i, int c) {
     row_ptr[i] = run;
-    run += counts[i];
-  }
+    run += c;
+  });
   if (t == kScanThreads - 1) row_ptr[n] = part[t];
   if (!row_order) return;
   const int64_t total = part[kScanThreads - 1];
 
   // P = rows longest first (counting sort)
-  for (int i = a; i < b; ++i) atomicAdd(&hist[min(counts[i], max_len)], 1);
-  __syncthreads();
-  if (t == 0) {   // bucket starts, longest bucket first
-    int acc = 0;
-    for (int c = max_len; c >= 0; --c) {
-      const int x = hist[c];
-      hist[c] = acc;
+  for_counts(counts, a, b, [&](int, int c) { atomicAdd(&hist[min(c, max_len)], 1); });
+  __syncthreads();   // hist complete; every read of part above is done
+  {   // bucket starts, longest bucket first: exclusive scan of hist taken from c = max_len down
+    const int nbk = max_len + 1;
+    const int per2 = (nbk + kScanThreads - 1) / kScanThreads;
+    const int q0 = min(nbk, t * per2), q1 = min(nbk, q0 + per2);
+    int sum = 0;
+    for (int q = q0; q < q1; ++q) sum += hist[max_len - q];
+    part[t] = sum;
+    __syncthreads();
+    block_scan(part);
+    int acc = part[t] - sum;
+    for (int q = q0; q < q1; ++q) {
+      const int x = hist[max_len - q];
+      hist[max_len - q] = acc;
       acc += x;
     }
   }
   __syncthreads();
-  for (int i = a; i < b; ++i) tmp[atomicAdd(&hist[min(counts[i], max_len)], 1)] = i;
+  for_counts(counts, a, b, [&](int i, int c) { tmp[atomicAdd(&hist[min(c, max_len)], 1)] = i; });
   __syncthreads();   // tmp complete: the barrier's fence orders the global writes
 
   // per-XCD ranks along P: counts of this thread's positions [a, b) of P
   int mine[kXcds];
 #pragma unroll
   for (int x = 0; x < kXcds; ++x) mine[x] = 0;
-  for (int p = a; p < b; ++p) {
-    const int r = tmp[p];
-    mine[xcd_of_row(row_ptr[r], counts[r], total)]++;
-  }
+  for_order(tmp, counts, row_ptr, a, b,
+            [&](int, int c, int start) { mine[xcd_of_row(start, c, total)]++; });
 #pragma unroll
   for (int x = 0; x < kXcds; ++x) xc[t][x] = mine[x];
   __syncthreads();
@@ -168,9 +222,8 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
     cap[x] = n / kXcds + (x < n % kXcds ? 1 : 0);      // positions dealt to XCD x
     deficit_start[x + 1] = deficit_start[x] + max(0, cap[x] - xtot[x]);
   }
-  for (int p = a; p < b; ++p) {
-    const int r = tmp[p];
-    const int x = xcd_of_row(row_ptr[r], counts[r], total);
+  for_order(tmp, counts, row_ptr, a, b, [&](int r, int c, int start) {
+    const int x = xcd_of_row(start, c, total);
     int pos;
     if (cnt[x] < cap[x]) {
       pos = kXcds * cnt[x] + x;
@@ -184,7 +237,7 @@ __global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t
     }
     cnt[x]++;
     row_order[pos] = r;
-  }
+  });
 }
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(

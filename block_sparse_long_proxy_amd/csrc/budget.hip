@@ -139,19 +139,36 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
   for (int z = 0; z < m; ++z) {            // probe blocks, in order
     const int I = nb - m + z;              // causal key blocks 0..I
     const float* L = lse + ((size_t)h * m + z) * nb * kBlock;
-    // 1. per-query normaliser (log2 domain), 4 partial merges per query.
+    // 1. per-query normaliser (log2 domain), 4 partial merges per query; the
+    //    partials of 8 blocks are loaded together (the loop is load-latency
+    //    bound otherwise), then folded in with one rescale.
     {
       const int i = t % kBlock, part = t / kBlock;   // kFinThreads == 4 * 128
       float mx = -INFINITY, sm = 0.f;
-      for (int J = part; J <= I; J += 4) {
-        const float x = L[(size_t)J * kBlock + i];
+      auto fold = [&](float x) {
         if (x > mx) {
           sm = sm * exp2f(mx - x) + 1.f;
           mx = x;
         } else {
           sm += exp2f(x - mx);
         }
+      };
+      int J = part;
+      for (; J + 28 <= I; J += 32) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = L[(size_t)(J + 4 * u) * kBlock + i];
+        float mloc = x[0];
+#pragma unroll
+        for (int u = 1; u < 8; ++u) mloc = fmaxf(mloc, x[u]);
+        if (mloc > mx) {
+          sm = (mx == -INFINITY) ? 0.f : sm * exp2f(mx - mloc);
+          mx = mloc;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sm += exp2f(x[u] - mx);
       }
+      for (; J <= I; J += 4) fold(L[(size_t)J * kBlock + i]);
       part_l[part * kBlock + i] = mx;
       part_s[part * kBlock + i] = sm;
     }
@@ -172,11 +189,28 @@ __global__ __launch_bounds__(kFinThreads) void budget_finalize_kernel(
     {
       const int wv = t >> 6, ln = t & 63, nw = kFinThreads / 64;
       const int rows = I == nb - 1 ? tail : kBlock;
-      for (int J = wv; J <= I; J += nw) {
+      // a query past a partial last block contributes nothing (its lse is
+      // replaced by +inf, so its exponentials are 0)
+      const float q0 = ln < rows ? qlse[ln] : INFINITY;
+      const float q1 = ln + 64 < rows ? qlse[ln + 64] : INFINITY;
+      int J = wv;
+      for (; J + 3 * nw <= I; J += 4 * nw) {   // four blocks' loads in flight together
+        float a[4], b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float* r = L + (size_t)(J + u * nw) * kBlock;
+          a[u] = r[ln];
+          b[u] = r[ln + 64];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float v = wave_sum(exp2f(a[u] - q0) + exp2f(b[u] - q1));
+          if (ln == 0) mass[J + u * nw] += v;
+        }
+      }
+      for (; J <= I; J += nw) {
         const float* r = L + (size_t)J * kBlock;
-        float v = (ln < rows ? exp2f(r[ln] - qlse[ln]) : 0.f) +
-                  (ln + 64 < rows ? exp2f(r[ln + 64] - qlse[ln + 64]) : 0.f);
-        v = wave_sum(v);
+        const float v = wave_sum(exp2f(r[ln] - q0) + exp2f(r[ln + 64] - q1));
         if (ln == 0) mass[J] += v;
       }
     }
