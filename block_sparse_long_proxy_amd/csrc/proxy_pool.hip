@@ -41,7 +41,18 @@ __global__ __launch_bounds__(256) void proxy_pool_kernel(
   float acc[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  for (int i = 0; i < count; ++i) {
+  // member heads in order, their loads issued four at a time
+  int i = 0;
+  for (; i + 4 <= count; i += 4) {
+    bf16x8 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const bf16x8*>(src + (size_t)(i + u) * head_elems);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)x[u][e];
+  }
+  for (; i < count; ++i) {
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + (size_t)i * head_elems);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += (float)x[e];
