@@ -22,7 +22,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 128;     // key/query block edge (tokens)
 constexpr int kWaves = 4;       // waves per workgroup in the tile kernels
@@ -128,93 +127,7 @@ __device__ __forceinline__ int acc_key(int t, int r) {
 }
 
 // ---------------------------------------------------------------------------
-// V^T tile in LDS: [D][128] bf16 (keys contiguous per dim row), stored in
-// 8-byte chunks (4 keys) with chunk c of row d at chunk (c ^ (d & 31)).
-__device__ __forceinline__ int vt_off(int d, int chunk8) {
-  return d * kBlock + ((chunk8 ^ (d & 31)) << 2);
-}
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi16, b.hi16)
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-// V tile staging into the transposed LDS layout.  Thread t owns the 8x8
-// (keys x dims) sub-block t (key group t / (D/8), dim group t % (D/8)); for
-// D = 64 only the first 128 threads have one.  The load half fetches the 8
-// rows, the store half transposes them with byte permutes and writes 8 dims x
-// 8 keys.
-template <int D>
-struct VStage {
-  u32x4 in[8];
-};
-
-template <int D>
-__device__ __forceinline__ bool vstage_active() {
-  return threadIdx.x < (kBlock / 8) * (D / 8);
-}
-
-template <int D>
-__device__ __forceinline__ void vstage_load(const __bf16* __restrict__ g, VStage<D>& st) {
-  constexpr int C = D / 8;
-  if (!vstage_active<D>()) return;
-  const int a = threadIdx.x / C, b = threadIdx.x % C;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    st.in[kk] = *reinterpret_cast<const u32x4*>(g + (size_t)(8 * a + kk) * D + 8 * b);
-}
-
-template <int D>
-__device__ __forceinline__ void vstage_store(const VStage<D>& st, __bf16* lds) {
-  constexpr int C = D / 8;
-  if (!vstage_active<D>()) return;
-  const int a = threadIdx.x / C, b = threadIdx.x % C;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    // out row: dim 8b+e, keys 8a..8a+7 -> 4 u32 words of 2 keys each
-    u32x2 w0, w1;
-    const int word = e >> 1;
-    if (e & 1) {
-      w0[0] = pack_hi(st.in[0][word], st.in[1][word]);
-      w0[1] = pack_hi(st.in[2][word], st.in[3][word]);
-      w1[0] = pack_hi(st.in[4][word], st.in[5][word]);
-      w1[1] = pack_hi(st.in[6][word], st.in[7][word]);
-    } else {
-      w0[0] = pack_lo(st.in[0][word], st.in[1][word]);
-      w0[1] = pack_lo(st.in[2][word], st.in[3][word]);
-      w1[0] = pack_lo(st.in[4][word], st.in[5][word]);
-      w1[1] = pack_lo(st.in[6][word], st.in[7][word]);
-    }
-    const int d = 8 * b + e;
-    *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a)) = w0;
-    *reinterpret_cast<u32x2*>(lds + vt_off(d, 2 * a + 1)) = w1;
-  }
-}
-
-// A operand of O^T += V^T . P^T: dims 32 m + l%32, the 8 keys that the C
-// layout of sub-tile t gives this lane for half `s2` (registers 8 s2 .. +7):
-// keys 32t + 16 s2 + 4 hi + {0..3} and the same + 8.
-__device__ __forceinline__ bf16x8 vtile_frag(const __bf16* lds, int m, int t, int s2) {
-  const int l = threadIdx.x & 63;
-  const int hi = l >> 5;
-  const int d = 32 * m + (l & 31);
-  const int c0 = (32 * t + 16 * s2 + 4 * hi) >> 2;
-  u32x2 x = *reinterpret_cast<const u32x2*>(lds + vt_off(d, c0));
-  u32x2 y = *reinterpret_cast<const u32x2*>(lds + vt_off(d, c0 + 2));
-  u32x4 v;
-  v[0] = x[0]; v[1] = x[1]; v[2] = y[0]; v[3] = y[1];
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// ---------------------------------------------------------------------------
 // Wave-level reductions (wave64).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 // Max over the 64 lanes of a wave without LDS traffic: DPP moves reduce each
 // row of 16 lanes, two row broadcasts fold the rows into lane 63, whose value
 // is returned (wave-uniform).
@@ -377,21 +290,7 @@ __device__ __forceinline__ void tile_load_lds_rows(const __bf16* __restrict__ g,
   }
 }
 
-// Copies one tile costs each thread when NW waves share it.
-template <int D, int NW>
-constexpr int tile_loads_per_thread() { return kBlock / (64 / (D / 8)) / NW; }
-
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// s_waitcnt vmcnt(N) with the other counters unconstrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).  Vector
-// memory operations complete in issue order, so this waits for all but the N
-// most recent loads of this thread.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
 
 // Element offset of (row, col) in a swizzled V tile.
 template <int D>
