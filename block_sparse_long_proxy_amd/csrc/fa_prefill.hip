@@ -6,14 +6,16 @@
 // restricted to kept blocks and j <= i, online softmax in fp32.
 //
 // One workgroup = one (head h, query block I); 4 waves x 32 queries.  For
-// every kept key block J (diagonal first, then descending J) the K tile and
-// the transposed V tile are staged through LDS and the wave computes
+// every kept key block J (diagonal first, then descending J) the K and V
+// tiles are staged through LDS and the wave computes
 //   S^T = K Q^T (32 MFMA 32x32x16), online softmax in registers,
 //   O^T += V^T P^T (32 MFMA).
 // K and V tiles are copied global -> LDS directly (no staging registers); the
 // copy of the next tile is issued before the MFMA phase it hides behind (V
 // during S + softmax, the next K during PV).  V stays row-major in LDS and is
-// read transposed with ds_read_b64_tr_b16.
+// read transposed with ds_read_b64_tr_b16.  A partial last block (128 does
+// not divide N) is read with its missing rows repeated from token N-1; the
+// rows of a fused batch are numbered sequence by sequence.
 #include <cmath>
 
 #include "pxa_device.hpp"
@@ -21,10 +23,6 @@
 
 namespace pxa {
 
-// Online-softmax update for one 128-key tile whose logits are in s[4]
-// (S^T layout: this lane's query, 64 of the tile's keys).  Masked entries are
-// -inf.  Returns the bf16 probabilities in the B-operand layout of the PV
-// MFMA and rescales the running output when the running max moved.
 // Row max of a tile (this lane's 64 logits, then the lane holding the same query).
 __device__ __forceinline__ float tile_row_max(const f32x16 (&s)[4]) {
   float mx = -INFINITY;
@@ -35,6 +33,11 @@ __device__ __forceinline__ float tile_row_max(const f32x16 (&s)[4]) {
   return fmaxf(mx, __shfl_xor(mx, 32, 64));
 }
 
+// Online-softmax update for one 128-key tile whose logits are in s[4]
+// (S^T layout: this lane's query, 64 of the tile's keys) with tile max mx.
+// Masked entries are -inf.  Returns the bf16 probabilities in the B-operand
+// layout of the PV MFMA and rescales the running output when the running max
+// moved.
 template <int D>
 __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], float mx, bf16x8 (&pb)[4][2],
                                                f32x16 (&oacc)[D / 32], float& m_run,
