@@ -15,7 +15,7 @@
 //   probe block); for each causal key block J the 128x128 logit tile
 //   S^T = K_J Q_T^T (MFMA) is reduced to a per-query log2-sum-exp2 over that
 //   block, lse[h][z][J][i].
-// Kernel 2 (budget_finalize_kernel): one workgroup per head; per probe block,
+// Kernel 2 (budget_finalize_kernel): one workgroup per (sequence, head); per probe block,
 //   merges the partials into each query's normaliser and adds the block
 //   masses; then sorts the last row's scores in LDS (bitonic, 64-bit keys)
 //   and scans the masses in rank order (fp32, fixed chunked order) for k_h.
