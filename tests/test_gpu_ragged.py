@@ -38,6 +38,14 @@ CASES = {
                           gammas=(0.95,), seed=26, n_needles=3),               # 97, nb = 1
     "n1_token": dict(num_heads=4, num_kv_heads=2, head_dim=128, seq_len=1, num_proxies=2,
                      gammas=(0.95,), seed=27, n_needles=1),                    # 1, nb = 1
+    # head layouts: multi-head (one KV head per query head) with a proxy per
+    # head, a single head, more proxies than KV heads
+    "mha_proxy_per_head": dict(num_heads=4, num_kv_heads=4, head_dim=64, seq_len=700,
+                               num_proxies=4, gammas=(0.9,), seed=28),         # 60
+    "one_head": dict(num_heads=1, num_kv_heads=1, head_dim=128, seq_len=513, num_proxies=1,
+                     gammas=(0.95,), seed=29),                                 # 1
+    "G8_Hkv2": dict(num_heads=8, num_kv_heads=2, head_dim=64, seq_len=900, num_proxies=8,
+                    gammas=(0.9,), seed=30),                                   # 4
 }
 
 _cache = {}
