@@ -12,7 +12,8 @@
 // compared with sets k_h to one value for every head (budget_fixed_kernel).
 //
 // Kernel 1 (budget_lse_kernel): one workgroup per (head, run of key blocks,
-//   probe block); for each causal key block J the 128x128 logit tile
+//   probe block); key tiles stream through a two-deep LDS ring filled by
+//   direct copies; for each causal key block J the 128x128 logit tile
 //   S^T = K_J Q_T^T (MFMA) is reduced to a per-query log2-sum-exp2 over that
 //   block, lse[h][z][J][i].
 // Kernel 2 (budget_finalize_kernel): one workgroup per (sequence, head); per probe block,
@@ -31,7 +32,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, float* __restrict__ lse,
     int H, int Hkv, int m, float scale_log2, const SeqTable t) {
-  __shared__ __attribute__((aligned(16))) __bf16 ks[kBlock * D];
+  // two-deep ring of K tiles, filled by direct global -> LDS copies (tile J+1
+  // lands while J is used)
+  __shared__ __attribute__((aligned(16))) __bf16 ks[2][kBlock * D];
   const int sid = (int)blockIdx.z / m;     // sequence of a fused batch
   const int z = (int)blockIdx.z % m;       // probe block z of m
   const int N = t.tok[sid + 1] - t.tok[sid];
@@ -52,15 +55,21 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
   bf16x8 qf[D / 16];
   // rows past a partial last block repeat token N-1 (excluded from the masses)
   load_qfrag<D>(q + ((size_t)h * N + (size_t)min(I * kBlock + qloc, N - 1)) * D, qf);
-  const __bf16* kb = k + (size_t)kvh * N * D;
+  const __bf16* kb = uniform_ptr(k + (size_t)kvh * N * D);
   float* out = lse + ((size_t)h * m + z) * nb * kBlock;
+  auto load = [&](int J, __bf16* buf) {   // only block nb-1 can be partial
+    const int rows = min(kBlock, N - J * kBlock);
+    if (rows < kBlock) tile_load_lds_rows<D, false>(kb + (size_t)J * kBlock * D, buf, rows);
+    else tile_load_lds<D, false>(kb + (size_t)J * kBlock * D, buf);
+  };
+  load(j0, ks[0]);
 
   for (int J = j0; J < j1; ++J) {
-    __syncthreads();
-    stage_ktile<D>(kb + (size_t)J * kBlock * D, ks, min(kBlock, N - J * kBlock));
-    __syncthreads();
+    wait_vmem();       // this thread's part of tile J (and the query fragments)
+    __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
+    if (J + 1 < j1) load(J + 1, ks[(J + 1 - j0) & 1]);
     f32x16 s[4];
-    tile_scores<D>(ks, qf, s);
+    tile_scores<D>(ks[(J - j0) & 1], qf, s);
     if (J == I) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -80,7 +89,8 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sum += exp2f(fmaf(s[t][r], scale_log2, -mb));
+      for (int r = 0; r < 16; ++r)   // v_exp_f32 directly: terms below 2^-126 flush to 0
+        sum += __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mb));
     sum += __shfl_xor(sum, 32, 64);
     if (l < 32) out[(size_t)J * kBlock + qloc] = mb + log2f(sum);
   }

@@ -21,7 +21,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 128;     // key/query block edge (tokens)
 constexpr int kWaves = 4;       // waves per workgroup in the tile kernels
@@ -46,47 +45,6 @@ template <int D>
 __device__ __forceinline__ int ktile_off(int row, int chunk) {
   constexpr int C = D / 8;
   return row * D + ((chunk ^ (row & (C - 1))) << 3);
-}
-
-// K tile staging, split so the global loads can be issued early and the LDS
-// stores done later: each thread moves kChunks 16-byte chunks of the
-// [128][D] tile (chunk c = it * kThreads + t: row c / (D/8), column c % (D/8)).
-template <int D>
-struct KStage {
-  static constexpr int kChunks = kBlock * (D / 8) / kThreads;
-  u32x4 r[kChunks];
-};
-
-// rows < 128: a partial tile; rows past the end repeat row rows-1.
-template <int D>
-__device__ __forceinline__ void kstage_load(const __bf16* __restrict__ g, KStage<D>& st,
-                                            int rows = kBlock) {
-  constexpr int C = D / 8;
-#pragma unroll
-  for (int it = 0; it < KStage<D>::kChunks; ++it) {
-    const int c = it * kThreads + threadIdx.x;
-    const int row = min(c / C, rows - 1);
-    st.r[it] = *reinterpret_cast<const u32x4*>(g + (size_t)row * D + (c % C) * 8);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void kstage_store(const KStage<D>& st, __bf16* lds) {
-  constexpr int C = D / 8;
-#pragma unroll
-  for (int it = 0; it < KStage<D>::kChunks; ++it) {
-    const int c = it * kThreads + threadIdx.x;
-    *reinterpret_cast<u32x4*>(lds + ktile_off<D>(c / C, c % C)) = st.r[it];
-  }
-}
-
-// Whole-tile copy (load + store) for kernels that do not pipeline.
-template <int D>
-__device__ __forceinline__ void stage_ktile(const __bf16* __restrict__ g, __bf16* lds,
-                                            int rows = kBlock) {
-  KStage<D> st;
-  kstage_load<D>(g, st, rows);
-  kstage_store<D>(st, lds);
 }
 
 // A operand (keys x d) of sub-tile `t` (32 keys) and k-step `s` (16 dims).
