@@ -1,6 +1,6 @@
 """Benchmark: ProxyAttn block-sparse causal prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload c2]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload llama8b_128k_g4]
 
 One step = one pass of the whole method over one layer of synthetic input
 already resident in HBM: proxy_pool -> proxy_score -> budget -> block_select
@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--workload", default="llama8b_128k_g4")
     ap.add_argument("--gamma", type=float, default=None)
     ap.add_argument("--dense-reps", type=int, default=3)
     ap.add_argument("--score-stride", type=int, default=1,
@@ -66,7 +66,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fa_prefill_sparse_c2.md")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fa_prefill_sparse_llama8b_128k_g4.md")
 KERNEL_SOURCES = ["block_sparse_long_proxy_amd/csrc/fa_prefill.hip",
                   "block_sparse_long_proxy_amd/csrc/pxa_device.hpp"]
 
@@ -288,8 +288,8 @@ def bench_batch(a, wl):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
-                          "part of it (the sharding design is described in DESIGN.md)",
+        print(json.dumps({"error": "only --gpus 1 is supported: the library runs the method on "
+                          "one GPU and has no multi-GPU path",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     import numpy as np

@@ -42,29 +42,29 @@ class WorkloadConfig:
 
 
 CONFIGS = {
-    "c0": WorkloadConfig(
-        name="c0", num_heads=4, num_kv_heads=2, head_dim=64, seq_len=2048,
+    "tiny_d64_2k": WorkloadConfig(
+        name="tiny_d64_2k", num_heads=4, num_kv_heads=2, head_dim=64, seq_len=2048,
         num_proxies=2, gammas=(0.95,), seed=0, rope_base=None,
         beta_range=(0.5, 4.0), n_needles=8, needle_query_frac=0.10, dtype="fp32",
         description="tiny fp32, GQA 4/2, d=64, N=2048, G=2"),
-    "c1": WorkloadConfig(
-        name="c1", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=32768,
+    "llama8b_32k_g1": WorkloadConfig(
+        name="llama8b_32k_g1", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=32768,
         num_proxies=1, gammas=(0.95,), seed=1, rope_base=500000.0,
         beta_range=(0.5, 4.0), n_needles=64, needle_query_frac=0.10,
         description="Llama-3.1-8B layer, N=32K, G=1"),
-    "c2": WorkloadConfig(
-        name="c2", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=131072,
+    "llama8b_128k_g4": WorkloadConfig(
+        name="llama8b_128k_g4", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=131072,
         num_proxies=4, gammas=(0.95,), seed=2, rope_base=500000.0,
         beta_range=(0.5, 4.0), n_needles=256, needle_query_frac=0.05,
         description="Llama-3.1-8B layer, N=128K, G=4"),
-    "c3": WorkloadConfig(
-        name="c3", num_heads=28, num_kv_heads=4, head_dim=128, seq_len=65536,
+    "qwen7b_64k_g4": WorkloadConfig(
+        name="qwen7b_64k_g4", num_heads=28, num_kv_heads=4, head_dim=128, seq_len=65536,
         num_proxies=4, gammas=(0.9,), seed=3, rope_base=1000000.0,
         beta_range=(0.5, 6.0), n_needles=128, needle_query_frac=0.05,
         group_latent_corr=0.3,
         description="Qwen2.5-7B layer, N=64K, G=4 (one proxy per GQA group)"),
-    "c4": WorkloadConfig(
-        name="c4", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=262144,
+    "long_256k_g8": WorkloadConfig(
+        name="long_256k_g8", num_heads=32, num_kv_heads=8, head_dim=128, seq_len=262144,
         num_proxies=8, gammas=(0.8, 0.9, 0.95), seed=4, rope_base=500000.0,
         beta_range=(1.0, 8.0), n_needles=512, needle_query_frac=0.02,
         description="long stress case, N=256K, G=8"),

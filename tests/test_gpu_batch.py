@@ -18,7 +18,7 @@ LENS = [384, 1024, 128, 640]
 
 
 def _seqs():
-    base = CONFIGS["c0"].with_(num_heads=8, num_kv_heads=2, head_dim=128, num_proxies=2,
+    base = CONFIGS["tiny_d64_2k"].with_(num_heads=8, num_kv_heads=2, head_dim=128, num_proxies=2,
                                gammas=(0.9,), rope_base=500000.0, dtype="bf16")
     return [generate(base.with_(name=f"seq{i}", seq_len=n, seed=40 + i)) for i, n in enumerate(LENS)]
 

@@ -21,7 +21,7 @@ from test_gpu_parity import case_data, run_pool, run_score, _empty  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["c0", "d128_rope_13blk", "G1_7heads", "G_gt_Hkv"]
+NAMES = ["tiny_d64_2k", "d128_rope_13blk", "G1_7heads", "G_gt_Hkv"]
 
 
 def _select_ex(cfg, budget, S, kh):
@@ -115,7 +115,7 @@ def test_ratio_count_float32_tie():
         assert lens[h, 9] == want
 
 
-@pytest.mark.parametrize("name", ["c0", "G1_7heads"])
+@pytest.mark.parametrize("name", ["tiny_d64_2k", "G1_7heads"])
 @pytest.mark.parametrize("budget", [Options.dynamic(3), Options.fixed(2), Options.ratio_of(0.25)],
                          ids=["dynamic3", "fixed2", "ratio0.25"])
 def test_prefill_ex_end_to_end(name, budget):
@@ -170,7 +170,7 @@ def test_strided_scores_parity(name, stride):
     assert np.all(got[fin] <= full[fin] + 1e-6 * np.maximum(np.abs(full[fin]), 1.0))
 
 
-@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+@pytest.mark.parametrize("name", ["tiny_d64_2k", "d128_rope_13blk"])
 def test_prefill_ex_with_query_stride(name):
     wl, cfg, q, k, v, dev = case_data(name)
     opts = Options.dynamic(score_stride=2)
@@ -197,7 +197,7 @@ def _mask_of(cfg, dev):
     return attn, rp, attn.col_idx.clone(), attn.row_order.clone()
 
 
-@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+@pytest.mark.parametrize("name", ["tiny_d64_2k", "d128_rope_13blk"])
 def test_skip_with_negligible_threshold_is_bit_identical(name):
     wl, cfg, q, k, v, dev = case_data(name)
     attn, rp, ci, order = _mask_of(cfg, dev)
@@ -223,7 +223,7 @@ def _robust_skip_rows(q, k, v, cfg, kv_of, rows_blocks, lam):
     return out
 
 
-@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk"])
+@pytest.mark.parametrize("name", ["tiny_d64_2k", "d128_rope_13blk"])
 @pytest.mark.parametrize("lam", [1e-3, 0.05, 1.0])
 def test_sparse_skip_parity(name, lam):
     wl, cfg, q, k, v, dev = case_data(name)

@@ -28,7 +28,7 @@ def _f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
-@pytest.fixture(scope="module", params=["c1", "c2"])
+@pytest.fixture(scope="module", params=["llama8b_32k_g1", "llama8b_128k_g4"])
 def run(request):
     wl = get_config(request.param)
     print(f"[fullsize] {wl.name}: generating N={wl.seq_len} H={wl.num_heads}", flush=True)

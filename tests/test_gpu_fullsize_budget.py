@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
 @pytest.fixture(scope="module")
 def data():
-    wl = get_config("c1")
+    wl = get_config("llama8b_32k_g1")
     print(f"[fullsize-budget] generating {wl.name} N={wl.seq_len}", flush=True)
     x = generate(wl)
     cfg = pxa.Config(wl.num_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.num_proxies, wl.gamma)

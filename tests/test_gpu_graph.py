@@ -16,7 +16,7 @@ from parity_util import gpu_bf16  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-BASE = CONFIGS["c0"].with_(num_heads=8, num_kv_heads=2, head_dim=128, num_proxies=2,
+BASE = CONFIGS["tiny_d64_2k"].with_(num_heads=8, num_kv_heads=2, head_dim=128, num_proxies=2,
                            gammas=(0.9,), rope_base=500000.0, dtype="bf16")
 
 

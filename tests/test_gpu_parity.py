@@ -20,10 +20,10 @@ from parity_util import (  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-BASE = CONFIGS["c0"]
+BASE = CONFIGS["tiny_d64_2k"]
 CASES = {
     # name: workload overrides (all bf16 on the GPU side)
-    "c0": dict(),
+    "tiny_d64_2k": dict(),
     "d128_rope_13blk": dict(num_heads=8, num_kv_heads=2, head_dim=128, seq_len=13 * 128,
                             num_proxies=2, gammas=(0.9,), seed=11, rope_base=500000.0,
                             n_needles=16, dtype="bf16"),
@@ -191,7 +191,7 @@ def test_sparse_attention_parity_on_gpu_mask(name):
     assert_outputs_close(host64(o), ref, name)
 
 
-@pytest.mark.parametrize("name", ["c0", "d128_rope_13blk", "single_block"])
+@pytest.mark.parametrize("name", ["tiny_d64_2k", "d128_rope_13blk", "single_block"])
 def test_dense_attention_parity(name):
     wl, cfg, q, k, v, dev = case_data(name)
     o = torch.empty_like(dev["q"])

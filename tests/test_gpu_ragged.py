@@ -23,7 +23,7 @@ from parity_util import (  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-BASE = CONFIGS["c0"]
+BASE = CONFIGS["tiny_d64_2k"]
 CASES = {
     # name: workload overrides; N mod 128 in the comment
     "n1000_d64": dict(seq_len=1000, seed=21),                                   # 104
