@@ -381,6 +381,12 @@ def test_ratio_count_rounds_the_product_to_float32():
     assert O.ratio_count(7, 1.0) == 8          # everything causal
     assert O.ratio_count(1000, 1e-6) == 1      # at least one block
     assert O.ratio_count(0, 0.2) == 1
+    # a fractional product rounds up (the count is a ceiling, not a floor or a
+    # round-to-nearest): 2.5 -> 3, 1.5 -> 2, 0.75 -> 1, 12.8 -> 13
+    assert O.ratio_count(9, 0.25) == 3
+    assert O.ratio_count(2, 0.5) == 2
+    assert O.ratio_count(2, 0.25) == 1
+    assert O.ratio_count(15, 0.8) == 13
 
 
 def test_ratio_selection_bruteforce():
