@@ -77,6 +77,17 @@ __device__ __forceinline__ void softmax_update(f32x16 (&s)[4], float mx, bf16x8 
   }
 }
 
+// Wave priorities (s_setprio) of the three phases of a step.  The two waves
+// sharing a SIMD (one from each of the CU's two workgroups) run out of phase;
+// when both can issue, the one in its softmax (the dependent VALU chain
+// between the products) goes first, then one in its PV products, and the QK^T
+// products of the other wave fill in behind.  Each switch also fences the
+// compiler's schedule, so the exponentials are computed before the PV
+// products rather than spread among them.
+constexpr int kPrioScores = 0;
+constexpr int kPrioSoftmax = 2;
+constexpr int kPrioPV = 1;
+
 // One pipeline step on key block J (tiles already in LDS / landing): S, the
 // softmax, then O += V P, issuing the copies of block Jn (knext / vnext NULL:
 // none; next_rows < 128: Jn is a partial last block).
@@ -93,6 +104,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
   f32x16 s[4];
   // S^T = K Q^T with the four K fragments of k-step ss+1 read while the four
   // products of step ss issue (scheduling barriers keep that order).
+  __builtin_amdgcn_s_setprio(kPrioScores);
   {
 #pragma unroll
     for (int t = 0; t < 4; ++t) s[t] = zero16();
@@ -119,6 +131,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
       for (int r = 0; r < 16; ++r)
         if (acc_key(t, r) > qloc) s[t][r] = -INFINITY;
   }
+  __builtin_amdgcn_s_setprio(kPrioSoftmax);
   bf16x8 pb[4][2];
   const float mx = tile_row_max(s);
   // m_run is -inf only before the first tile, where the comparison is false
@@ -132,6 +145,7 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
     else tile_load_lds<D, false>(knext, ks);
   }
 
+  __builtin_amdgcn_s_setprio(kPrioPV);
   if (!skip) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -142,6 +156,10 @@ __device__ __forceinline__ void fa_step(const __bf16* ks_lds, const __bf16* vs_l
           oacc[m] = mfma32(vfrag_tr<D>(vs_lds, m, t, s2), pb[t][s2], oacc[m]);
   }
 
+  // Same priority again: the switch keeps every PV product ahead of the copy
+  // wait and the barrier (left alone, the compiler sinks the last products
+  // past them, which measured slower).
+  __builtin_amdgcn_s_setprio(kPrioPV);
   wait_vmem();                   // this thread's part of K(Jn) has landed
   __syncthreads();               // K(Jn) visible; every wave is done with the V tile
   if (vnext) {
