@@ -36,6 +36,11 @@
 namespace pxa {
 
 constexpr int kScoreBufs = 2;                  // K tile in use + the next one in flight
+// Wave priorities (s_setprio): a wave taking its block maxima (a short
+// dependent VALU chain before the next barrier) issues ahead of the other
+// workgroup's wave on the same SIMD, whose products fill in behind.
+constexpr int kPrioProducts = 0;
+constexpr int kPrioMax = 1;
 
 // STRIDE s: the block's queries at offsets s-1, 2s-1, ..., 127 are scored
 // (128/s of them, in QC = 4/s chunks of 32); s = 1 scores every query.
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     if (J > J0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
     const __bf16* cur = kt[J % kScoreBufs];
     f32x16 acc[4];
+    __builtin_amdgcn_s_setprio(kPrioProducts);
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = zero16();
     // The fragment of k-step s+1 is read before the four products of step s
@@ -161,6 +167,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       __builtin_amdgcn_sched_barrier(0);
       a = an;
     }
+    __builtin_amdgcn_s_setprio(kPrioMax);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int Ir = I0 - r;
