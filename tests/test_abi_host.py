@@ -197,6 +197,22 @@ def test_validate_config_codes(kw, code):
     assert pxa.pxa_validate_config(_good(**kw)) == code
 
 
+def test_size_limits_at_their_boundaries():
+    """N <= 524288, and the causal blocks of all heads, H nb (nb+1) / 2, must
+    fit the int32 CSR entries: at nb = 4096 that is 255 heads, not 256."""
+    one_kv = dict(num_kv_heads=1, num_proxies=1)
+    assert pxa.pxa_validate_config(_good(seq_len=524288, **one_kv)) == B.PXA_OK
+    assert pxa.pxa_validate_config(_good(seq_len=524289, **one_kv)) == B.PXA_EUNSUPPORTED
+    assert pxa.pxa_validate_config(_good(seq_len=524288, num_heads=255, **one_kv)) == B.PXA_OK
+    assert pxa.pxa_validate_config(_good(seq_len=524288, num_heads=256, **one_kv)) == B.PXA_EUNSUPPORTED
+    assert pxa.pxa_validate_config(_good(seq_len=524160, num_heads=256, **one_kv)) == B.PXA_OK  # 4095 blocks
+    cfg = _good(seq_len=524288, num_heads=255, **one_kv)
+    assert pxa.pxa_max_col_entries(cfg) == 255 * 4096 * 4097 // 2
+    L = pxa.pxa_get_workspace_layout(cfg)
+    assert L.col_idx + 4 * pxa.pxa_max_col_entries(cfg) <= L.row_order <= L.total
+    assert L.total == pxa.pxa_workspace_bytes(cfg) > 8 * 2**30   # sizes in 64-bit arithmetic
+
+
 def test_invalid_config_has_zero_sizes():
     bad = _good(head_dim=96)
     assert pxa.pxa_workspace_bytes(bad) == 0

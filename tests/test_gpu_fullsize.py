@@ -1,4 +1,6 @@
-"""GPU parity at the full workload sizes (32K tokens with one proxy; 128K with four).
+"""GPU parity at the full workload sizes (32K tokens with one proxy; 128K with
+four) and at the longest sequence the library accepts (524,288 tokens, 4096
+blocks, with four query heads on one KV head so that it stays quick).
 
 pxa_prefill runs exactly as the benchmark times it.  The oracle checks what
 it can compute one piece at a time: proxies of sampled tokens, proxy scores
@@ -28,9 +30,16 @@ def _f64(bits):
     return bf16_bits_to_f32(bits).astype(np.float64)
 
 
-@pytest.fixture(scope="module", params=["llama8b_32k_g1", "llama8b_128k_g4"])
+# The maximum length: the row arrays, the 4096-key sorts and the largest
+# offsets of every kernel at their limit.
+MAXLEN = get_config("llama8b_32k_g1").with_(
+    name="maxlen_512k_h4", seq_len=524288, num_heads=4, num_kv_heads=1, num_proxies=1,
+    n_needles=256, seed=7)
+
+
+@pytest.fixture(scope="module", params=["llama8b_32k_g1", "llama8b_128k_g4", "maxlen_512k_h4"])
 def run(request):
-    wl = get_config(request.param)
+    wl = MAXLEN if request.param == MAXLEN.name else get_config(request.param)
     print(f"[fullsize] {wl.name}: generating N={wl.seq_len} H={wl.num_heads}", flush=True)
     x = generate(wl)
     cfg = pxa.Config(wl.num_heads, wl.num_kv_heads, wl.seq_len, wl.head_dim, wl.num_proxies, wl.gamma)
