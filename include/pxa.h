@@ -53,7 +53,7 @@ extern "C" {
 enum {
   PXA_OK = 0,
   PXA_EINVAL = -1,       /* inconsistent shape, grouping, gamma or scale     */
-  PXA_EUNSUPPORTED = -2, /* d not 64/128, block not 128, N too big              */
+  PXA_EUNSUPPORTED = -2, /* d not 64/128, block not 128, N or H*nb^2 too big   */
   PXA_ENULL = -3,        /* a required pointer is NULL                       */
   PXA_EALIGN = -4,       /* a pointer violates its alignment requirement    */
   PXA_EWORKSPACE = -5,   /* workspace smaller than the *_workspace_bytes query */
@@ -65,7 +65,10 @@ typedef struct pxa_config {
   int32_t num_heads;     /* H  >= 1                                              */
   int32_t num_kv_heads;  /* Hkv >= 1, H % Hkv == 0                               */
   int32_t seq_len;       /* N, 1 <= N <= 524288; nb = ceil(N/128) blocks, the
-                            last one partial when 128 does not divide N          */
+                            last one partial when 128 does not divide N; the
+                            causal blocks of all heads, H*nb*(nb+1)/2, must fit
+                            the int32 CSR (at nb = 4096: H <= 255), else
+                            PXA_EUNSUPPORTED                                     */
   int32_t head_dim;      /* d, 64 or 128                                         */
   int32_t block;         /* must be 128 (blog post section 2: 128x128 blocks)    */
   int32_t num_proxies;   /* G: H % G == 0 and (Hkv % G == 0 or G % Hkv == 0)     */
