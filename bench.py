@@ -186,7 +186,20 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_k
                    f"the full step by its work units (tokens, causal tiles, heads, rows, kept tiles)"),
         "stage_s": {k: round(v, 3) for k, v in est.items()},
         "wall_s": round(time.perf_counter() - t_all, 2),
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model():
+    """Model name of the host CPU (first entry of /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def bench_batch(a, wl):
