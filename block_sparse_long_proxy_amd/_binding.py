@@ -227,6 +227,33 @@ def _tp(x, kind, name):
     return _ptr(x, None if isinstance(x, int) or x is None else _dt(kind), name)
 
 
+def _needs(cfg: Config, tokens: Optional[int] = None) -> dict:
+    """Elements each array argument must hold for cfg (tokens: the total of a batch)."""
+    H, Hkv, G, d, nb = cfg.num_heads, cfg.num_kv_heads, cfg.num_proxies, cfg.head_dim, cfg.nb
+    N = cfg.seq_len if tokens is None else tokens
+    return dict(q=H * N * d, o=H * N * d, k=Hkv * N * d, v=Hkv * N * d, qbar=G * N * d,
+                kbar=G * N * d, scores=G * nb * nb, k_h=H, masses=H * nb, row_ptr=H * nb + 1,
+                row_order=H * nb, col_idx=H * nb * (nb + 1) // 2)
+
+
+def _check_sizes(cfg: Config, tokens: Optional[int] = None, ws=None, ws_bytes=None, **arrays):
+    """Refuse torch tensors smaller than the call reads or writes (the kernels
+    trust the sizes the configuration implies; raw int addresses are the
+    caller's responsibility).  Skipped for an invalid configuration, which the
+    library itself reports."""
+    import torch
+    if load_library().pxa_validate_config(ctypes.byref(cfg.c())) != PXA_OK:
+        return
+    need = _needs(cfg, tokens)
+    for name, x in arrays.items():
+        if isinstance(x, torch.Tensor) and x.numel() < need[name]:
+            raise ValueError(f"{name}: {x.numel()} elements, the configuration needs {need[name]}")
+    if isinstance(ws, torch.Tensor) and ws_bytes is not None:
+        if ws_bytes > ws.numel() * ws.element_size():
+            raise ValueError(f"ws_bytes {ws_bytes} exceeds the workspace tensor "
+                             f"({ws.numel() * ws.element_size()} bytes)")
+
+
 # ---------------------------------------------------------------- queries
 def pxa_abi_version() -> int:
     return load_library().pxa_abi_version()
@@ -271,6 +298,7 @@ def _nbytes(ws, ws_bytes):
 
 
 def pxa_prefill(cfg: Config, q, k, v, o, ws, ws_bytes=None, stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, o=o, ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_prefill(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"), _tp(v, "bf16", "v"),
         _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes), _stream(stream)),
@@ -278,12 +306,14 @@ def pxa_prefill(cfg: Config, q, k, v, o, ws, ws_bytes=None, stream=None) -> None
 
 
 def pxa_proxy_pool(cfg: Config, q, k, qbar, kbar, stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, qbar=qbar, kbar=kbar)
     _check(load_library().pxa_proxy_pool(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"), _stream(stream)), "pxa_proxy_pool")
 
 
 def pxa_proxy_score(cfg: Config, qbar, kbar, scores, stream=None) -> None:
+    _check_sizes(cfg, qbar=qbar, kbar=kbar, scores=scores)
     _check(load_library().pxa_proxy_score(
         ctypes.byref(cfg.c()), _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"),
         _tp(scores, "f32", "scores"), _stream(stream)), "pxa_proxy_score")
@@ -291,6 +321,8 @@ def pxa_proxy_score(cfg: Config, qbar, kbar, scores, stream=None) -> None:
 
 def pxa_budget_estimate(cfg: Config, q, k, scores, k_h, masses, ws, ws_bytes=None,
                         stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, scores=scores, k_h=k_h, masses=masses,
+                 ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_budget_estimate(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"), _tp(masses, "f32", "masses"),
@@ -299,6 +331,8 @@ def pxa_budget_estimate(cfg: Config, q, k, scores, k_h, masses, ws, ws_bytes=Non
 
 def pxa_block_select(cfg: Config, scores, k_h, row_ptr, col_idx, ws, ws_bytes=None,
                      stream=None, row_order=None) -> None:
+    _check_sizes(cfg, scores=scores, k_h=k_h, row_ptr=row_ptr, col_idx=col_idx,
+                 row_order=row_order, ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_block_select(
         ctypes.byref(cfg.c()), _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"),
         _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
@@ -308,6 +342,7 @@ def pxa_block_select(cfg: Config, scores, k_h, row_ptr, col_idx, ws, ws_bytes=No
 
 def pxa_sparse_prefill(cfg: Config, q, k, v, row_ptr, col_idx, o, stream=None,
                        row_order=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, row_ptr=row_ptr, row_order=row_order, o=o)
     _check(load_library().pxa_sparse_prefill(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"), _tp(v, "bf16", "v"),
         _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
@@ -316,6 +351,7 @@ def pxa_sparse_prefill(cfg: Config, q, k, v, row_ptr, col_idx, o, stream=None,
 
 
 def pxa_dense_prefill(cfg: Config, q, k, v, o, stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, o=o)
     _check(load_library().pxa_dense_prefill(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"), _tp(v, "bf16", "v"),
         _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill")
@@ -324,6 +360,7 @@ def pxa_dense_prefill(cfg: Config, q, k, v, o, stream=None) -> None:
 # ---------------------------------------------------------------- method variants
 def pxa_proxy_score_ex(cfg: Config, opts: Optional[Options], qbar, kbar, scores,
                        stream=None) -> None:
+    _check_sizes(cfg, qbar=qbar, kbar=kbar, scores=scores)
     _check(load_library().pxa_proxy_score_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"),
         _tp(scores, "f32", "scores"), _stream(stream)), "pxa_proxy_score_ex")
@@ -351,6 +388,7 @@ def pxa_budget_workspace_bytes_ex(cfg: Config, opts: Optional[Options]) -> int:
 
 def pxa_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, ws, ws_bytes=None,
                    stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, o=o, ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_prefill_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
@@ -359,6 +397,8 @@ def pxa_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, ws, ws_byte
 
 def pxa_budget_estimate_ex(cfg: Config, opts: Optional[Options], q, k, scores, k_h, masses, ws,
                            ws_bytes=None, stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, scores=scores, k_h=k_h, masses=masses,
+                 ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_budget_estimate_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"), _tp(masses, "f32", "masses"),
@@ -368,6 +408,8 @@ def pxa_budget_estimate_ex(cfg: Config, opts: Optional[Options], q, k, scores, k
 
 def pxa_block_select_ex(cfg: Config, opts: Optional[Options], scores, k_h, row_ptr, col_idx, ws,
                         ws_bytes=None, stream=None, row_order=None) -> None:
+    _check_sizes(cfg, scores=scores, k_h=k_h, row_ptr=row_ptr, col_idx=col_idx,
+                 row_order=row_order, ws=ws, ws_bytes=ws_bytes)
     _check(load_library().pxa_block_select_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(scores, "f32", "scores"), _tp(k_h, "i32", "k_h"),
         _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
@@ -377,6 +419,7 @@ def pxa_block_select_ex(cfg: Config, opts: Optional[Options], scores, k_h, row_p
 
 def pxa_sparse_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, row_ptr, col_idx, o,
                           stream=None, row_order=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, row_ptr=row_ptr, row_order=row_order, o=o)
     _check(load_library().pxa_sparse_prefill_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(row_ptr, "i32", "row_ptr"), _tp(col_idx, "i32", "col_idx"),
@@ -385,6 +428,7 @@ def pxa_sparse_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, row_ptr
 
 
 def pxa_dense_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, stream=None) -> None:
+    _check_sizes(cfg, q=q, k=k, v=v, o=o)
     _check(load_library().pxa_dense_prefill_ex(
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _stream(stream)), "pxa_dense_prefill_ex")
@@ -415,6 +459,8 @@ def pxa_prefill_batch(cfg: Config, opts: Optional[Options], seq_lens, q, k, v, o
     """seq_lens: host list of per-sequence token counts; q/k/v/o: the per-sequence
     [heads][N_s][d] blocks stored one after another (flat bf16 tensors are fine).
     Fused when ws holds pxa_batch_workspace_bytes, else one sequence at a time."""
+    _check_sizes(cfg, tokens=sum(int(x) for x in seq_lens), q=q, k=k, v=v, o=o, ws=ws,
+                 ws_bytes=ws_bytes)
     n, arr = _lens(seq_lens)
     _check(load_library().pxa_prefill_batch(
         ctypes.byref(cfg.c()), _bref(opts), n, arr, _tp(q, "bf16", "q"),

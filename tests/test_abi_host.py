@@ -296,9 +296,42 @@ def test_strerror_covers_codes():
 def test_binding_refuses_cpu_tensors():
     import torch
     cfg = _good()
-    t = torch.zeros(8, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
+    t = torch.zeros(cfg.num_heads * cfg.seq_len * cfg.head_dim, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
         pxa.pxa_dense_prefill(cfg, t, t, t, t, stream=0)
+
+
+def test_binding_refuses_tensors_smaller_than_the_configuration():
+    """The kernels trust the sizes the configuration implies, so the binding
+    refuses a torch tensor that is too small before anything is launched (the
+    size check comes before the device check, so CPU tensors show it here)."""
+    import torch
+    cfg = _good()
+    H, Hkv, N, d, G, nb = (cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim,
+                           cfg.num_proxies, cfg.nb)
+    bf = lambda n: torch.zeros(n, dtype=torch.bfloat16)  # noqa: E731
+    q, kv = bf(H * N * d), bf(Hkv * N * d)
+    with pytest.raises(ValueError, match="^q: "):
+        pxa.pxa_dense_prefill(cfg, bf(H * N * d - 1), kv, kv, q, stream=0)
+    with pytest.raises(ValueError, match="^v: "):
+        pxa.pxa_sparse_prefill(cfg, q, kv, bf(Hkv * (N - 128) * d), torch.zeros(H * nb + 1, dtype=torch.int32),
+                               torch.zeros(1, dtype=torch.int32), q, stream=0)
+    with pytest.raises(ValueError, match="^scores: "):
+        pxa.pxa_proxy_score(cfg, bf(G * N * d), bf(G * N * d),
+                            torch.zeros(G * nb * nb - 1, dtype=torch.float32), stream=0)
+    with pytest.raises(ValueError, match="^col_idx: "):
+        pxa.pxa_block_select(cfg, torch.zeros(G * nb * nb), torch.zeros(H, dtype=torch.int32),
+                             torch.zeros(H * nb + 1, dtype=torch.int32),
+                             torch.zeros(H * nb, dtype=torch.int32), torch.zeros(16, dtype=torch.uint8),
+                             stream=0)
+    with pytest.raises(ValueError, match="^ws_bytes"):
+        pxa.pxa_prefill(cfg, q, kv, kv, q, torch.zeros(64, dtype=torch.uint8), ws_bytes=1 << 20,
+                        stream=0)
+    lens = [300, 1000]
+    with pytest.raises(ValueError, match="^o: "):
+        pxa.pxa_prefill_batch(cfg, None, lens, bf(H * 1300 * d), bf(Hkv * 1300 * d),
+                              bf(Hkv * 1300 * d), bf(H * 1299 * d), torch.zeros(64, dtype=torch.uint8),
+                              stream=0)
 
 
 def test_product_path_does_not_import_oracle():
