@@ -129,3 +129,32 @@ def test_fused_batch_intermediates_are_each_sequences_own():
     order = _i32(ws, L.row_order, H * blk).cpu().numpy()
     full_rp = _i32(ws, L.row_ptr, H * blk + 1).cpu().numpy()
     check_schedule(order, full_rp)
+
+
+@pytest.mark.parametrize("H,Hkv,d,G", [(4, 2, 64, 2), (8, 2, 128, 8), (4, 4, 128, 4)],
+                         ids=["d64", "G_gt_Hkv", "proxy_per_head"])
+def test_fused_batch_of_other_shapes_and_ragged_lengths(H, Hkv, d, G):
+    """Other layer shapes (head dim 64, more proxies than KV heads, a proxy per
+    head) with partial last blocks of every kind, fused: each sequence's output
+    equals its own call bit for bit."""
+    lens = [1, 129, 700, 2047, 128, 97]
+    base = CONFIGS["tiny_d64_2k"].with_(num_heads=H, num_kv_heads=Hkv, head_dim=d, num_proxies=G,
+                                        gammas=(0.9,), rope_base=500000.0, dtype="bf16")
+    xs = [generate(base.with_(name=f"shape{i}", seq_len=n, seed=60 + i, n_needles=min(n, 8)))
+          for i, n in enumerate(lens)]
+    cfg = pxa.Config(H, Hkv, max(lens), d, G, 0.9)
+    flat = {n: torch.cat([gpu_bf16(x[n]).reshape(-1) for x in xs]) for n in ("q", "k", "v")}
+    o = torch.full_like(flat["q"], float("nan"))
+    ws = torch.empty(pxa.pxa_batch_workspace_bytes(cfg, None, lens), dtype=torch.uint8,
+                     device="cuda")
+    print(f"[batch shapes] H={H} Hkv={Hkv} d={d} G={G} lens={lens}", flush=True)
+    pxa.pxa_prefill_batch(cfg, None, lens, flat["q"], flat["k"], flat["v"], o, ws)
+    torch.cuda.synchronize()
+    off = 0
+    for x, n in zip(xs, lens):
+        ref = pxa.ProxyAttn(pxa.Config(H, Hkv, n, d, G, 0.9))(gpu_bf16(x["q"]), gpu_bf16(x["k"]),
+                                                              gpu_bf16(x["v"]))
+        torch.cuda.synchronize()
+        assert torch.equal(o[off:off + H * n * d].view(H, n, d), ref), f"sequence of {n} tokens"
+        off += H * n * d
+    assert off == o.numel()
