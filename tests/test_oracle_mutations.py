@@ -51,6 +51,12 @@ MUTATIONS = {
     "skip_any_query": ("np.all(tg - mg < log_thr)", "np.any(tg - mg < log_thr)"),
     "bf16_truncation": ("np.round(m * 256.0)", "np.floor(m * 256.0)"),
     "density_diagonal_whole": ("keep.sum() - 0.5 * diag", "keep.sum()"),
+    "blocks_floor": ("return -(-N // block)", "return max(1, N // block)"),
+    "partial_block_past_the_end": ("np.arange(I * block, min((I + 1) * block, N))",
+                                   "np.arange(I * block, (I + 1) * block)"),
+    "group_kv_first_only": ("return sorted({kv_head_of(h, H, Hkv) for h in group_query_heads(g, H, G)})",
+                            "return [kv_head_of(g * (H // G), H, Hkv)]"),
+    "bf16_ties_up": ("np.round(m * 256.0)", "np.floor(m * 256.0 + 0.5)"),
 }
 
 # The pin tests run against the copy: it is imported before pytest starts, so
