@@ -29,13 +29,16 @@ B = 128
 
 
 def parse():
+    from synth.configs import CONFIGS
     ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b_128k_g4")
-    ap.add_argument("--gamma", type=float, default=None)
-    ap.add_argument("--dense-reps", type=int, default=3)
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1 is supported)")
+    ap.add_argument("--steps", type=int, default=10, help="timed steps (whole method per step)")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed steps before the timed ones")
+    ap.add_argument("--workload", default="llama8b_128k_g4", choices=sorted(CONFIGS),
+                    help="layer shape, length, proxies and gamma of the synthetic input")
+    ap.add_argument("--gamma", type=float, default=None, help="override the workload's gamma")
+    ap.add_argument("--dense-reps", type=int, default=3,
+                    help="timed runs of the dense kernel (the speedup denominator)")
     ap.add_argument("--score-stride", type=int, default=1,
                     help="sequence-level skip of the proxy scoring: score every s-th query "
                          "(1, 2 or 4; 1 = every query, the default)")
@@ -51,7 +54,8 @@ def parse():
                     help="comma-separated sequence lengths: time one pxa_prefill_batch call over "
                          "them (heads, dims, proxies and gamma of --workload) against one "
                          "pxa_prefill_ex call per sequence, and print that line instead")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the timed sample of the CPU oracle")
     ap.add_argument("--no-sdpa", action="store_true",
                     help="skip the context timing of torch's flash SDPA at the same shape")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0,
