@@ -26,9 +26,9 @@ function that applies it):
   distinct KV heads those query heads use (K);
 * token-level score = scale * q.k logit (no softmax), causal entries only;
   blocks above the diagonal are -inf and never selectable;
-* the proxies are stored as bfloat16 and the block scores as float32: the
-  ranking is an integer decision, so it is taken on the values in the
-  precision the GPU path stores them in (round-to-nearest-even);
+* every quantity is exact to float64: the proxies are the plain means and
+  the block scores and the ranking are float64 (no storage precision of any
+  implementation is modelled; the mask tolerance of a comparison covers it);
 * ranking order: score descending, block index ascending on ties;
 * budget: the last query block's exact causal softmax, averaged over its
   queries, summed per key block, accumulated (float64) along the group's
@@ -88,30 +88,16 @@ def block_tokens(I: int, block: int, N: int) -> np.ndarray:
     return np.arange(I * block, min((I + 1) * block, N))
 
 
-def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round to the nearest bfloat16 value (8 significant bits), ties to even.
-
-    Works on the float64 significand: frexp gives x = m * 2**e with
-    0.5 <= |m| < 1; bfloat16 keeps 8 significant bits, i.e. m to a multiple of
-    2**-8.  numpy's round() is round-half-to-even.  Valid for the normal range
-    (the workloads never reach subnormals or overflow).
-    """
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)
-    return np.ldexp(np.round(m * 256.0) / 256.0, e)
-
-
 # --------------------------------------------------------------------------
 # step 1: head pooling
 # --------------------------------------------------------------------------
-def proxy_pool(q: np.ndarray, k: np.ndarray, G: int, to_bf16: bool = True):
+def proxy_pool(q: np.ndarray, k: np.ndarray, G: int):
     """Proxy heads: mean of Q over each group's query heads, of K over its KV heads.
 
     Blog post section 4, step 1 "Head Pooling" (aggregate Q and K over the head
     dimension inside a group to get one proxy head); section 3 calls it a
     simple pooling.  Mean is the reading taken (a positive rescaling, so the
-    ranking equals that of a sum).  With to_bf16 the proxies are rounded once
-    to bfloat16, the precision the scores are computed from on the GPU.
+    ranking equals that of a sum).  Exact float64 means, not rounded.
 
     q: [H, N, d], k: [Hkv, N, d] -> qbar, kbar: [G, N, d] float64.
     """
@@ -126,8 +112,6 @@ def proxy_pool(q: np.ndarray, k: np.ndarray, G: int, to_bf16: bool = True):
         kh = group_kv_heads(g, H, Hkv, G)
         qbar[g] = np.mean(np.asarray(q[qh], dtype=np.float64), axis=0)
         kbar[g] = np.mean(np.asarray(k[kh], dtype=np.float64), axis=0)
-    if to_bf16:
-        qbar, kbar = round_bf16(qbar), round_bf16(kbar)
     return qbar, kbar
 
 
@@ -190,9 +174,9 @@ def rank_blocks(S_row: np.ndarray, I: int) -> np.ndarray:
 
     Blog post section 4, step 1 "Block Ranking".  The pages give no tie rule;
     the reading is: score descending, then block index ascending.  Scores are
-    compared as the float32 values the GPU path stores.
+    compared as given (float64).
     """
-    s = np.asarray(S_row[: I + 1], dtype=np.float32).astype(np.float64)
+    s = np.asarray(S_row[: I + 1], dtype=np.float64)
     J = np.arange(I + 1)
     return np.lexsort((J, -s))
 
@@ -448,8 +432,7 @@ def causal_keep(H: int, nb: int) -> np.ndarray:
 # whole pipeline
 # --------------------------------------------------------------------------
 def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
-             block: int = 128, scale: Optional[float] = None,
-             proxies_bf16: bool = True, with_output: bool = True,
+             block: int = 128, scale: Optional[float] = None, with_output: bool = True,
              budget: Optional[Dict] = None, score_stride: int = 1) -> Dict[str, np.ndarray]:
     """Run every step in order and return all intermediates.
 
@@ -467,7 +450,7 @@ def pipeline(q: np.ndarray, k: np.ndarray, v: np.ndarray, G: int, gamma: float,
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
-    qbar, kbar = proxy_pool(q, k, G, to_bf16=proxies_bf16)
+    qbar, kbar = proxy_pool(q, k, G)
     S = proxy_scores(qbar, kbar, block, scale, query_stride=score_stride)
     mode = budget["mode"]
     if mode == "dynamic":

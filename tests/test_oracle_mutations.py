@@ -36,6 +36,11 @@ MUTATIONS = {
                  "kbar[g] = np.sum(np.asarray(k[kh], dtype=np.float64), axis=0)"),
     "tie_break_reversed": ("return np.lexsort((J, -s))", "return np.lexsort((-J, -s))"),
     "ranking_ascending": ("return np.lexsort((J, -s))", "return np.lexsort((J, s))"),
+    "ranking_in_float32": ("s = np.asarray(S_row[: I + 1], dtype=np.float64)",
+                           "s = np.asarray(S_row[: I + 1], dtype=np.float32).astype(np.float64)"),
+    "pool_rounded_bf16": ("        kbar[g] = np.mean(np.asarray(k[kh], dtype=np.float64), axis=0)\n    return",
+                          "        kbar[g] = np.mean(np.asarray(k[kh], dtype=np.float64), axis=0)\n"
+                          "    qbar = qbar.astype(np.float32).astype(np.float64)\n    return"),
     "budget_strict": ("if cum >= gamma:", "if cum > gamma:"),
     "budget_off_by_one": ("order[: min(int(k), I + 1)]", "order[: min(int(k) + 1, I + 1)]"),
     "no_diagonal": ("    kept.add(I)\n", ""),
@@ -49,14 +54,12 @@ MUTATIONS = {
     "attn_no_scale": ("L = scale * (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)",
                       "L = (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)"),
     "skip_any_query": ("np.all(tg - mg < log_thr)", "np.any(tg - mg < log_thr)"),
-    "bf16_truncation": ("np.round(m * 256.0)", "np.floor(m * 256.0)"),
     "density_diagonal_whole": ("keep.sum() - 0.5 * diag", "keep.sum()"),
     "blocks_floor": ("return -(-N // block)", "return max(1, N // block)"),
     "partial_block_past_the_end": ("np.arange(I * block, min((I + 1) * block, N))",
                                    "np.arange(I * block, (I + 1) * block)"),
     "group_kv_first_only": ("return sorted({kv_head_of(h, H, Hkv) for h in group_query_heads(g, H, G)})",
                             "return [kv_head_of(g * (H // G), H, Hkv)]"),
-    "bf16_ties_up": ("np.round(m * 256.0)", "np.floor(m * 256.0 + 0.5)"),
 }
 
 # The pin tests run against the copy: it is imported before pytest starts, so
