@@ -106,67 +106,88 @@ def profiled_traffic(workload):
         return None
 
 
-def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_kind="dynamic",
-                 score_stride=1):
-    """Time the CPU oracle on a bounded sample and scale it to the full step.
+def cpu_baseline(cfg, x, samples, n_kept, gpu_csr, budget_s=20.0, last_blocks=1,
+                 budget_kind="dynamic", score_stride=1, gamma=None, budget_param=None):
+    """Time the CPU oracle (float64 NumPy, as it stands) and scale it to the full step.
 
-    Sample: a token slice of the pooling, three query-block rows of the proxy
-    scores (scaled by causal tiles), the last-block masses of one head (scaled
-    by heads), ranking + selection of three rows (scaled by rows), and sparse
-    attention of a few (head, row) pairs on the GPU's own mask (scaled by kept
-    tiles).  `samples`: list of (h, I, kept block indices).
+    Pooling and, for the dynamic budget, the masses of every head are timed in
+    full (heads spread over a thread pool); the proxy scores of a sample of
+    rows of every proxy (scaled by causal tiles), the selection of those rows
+    (scaled by rows) and the sparse attention of a few (head, row) pairs on the
+    GPU's own mask (scaled by kept tiles) are sampled.  The same oracle
+    intermediates then check the GPU's mask on the sampled rows against the
+    oracle's own chain (its proxies, scores, ranking and budgets).
+    `samples`: list of (h, I, kept block indices); gpu_csr: (row_ptr, col_idx, k_h);
+    budget_param: the blocks of a fixed budget or the ratio of a ratio budget.
     """
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import proxyattn as O
     from synth import bf16_bits_to_f32
 
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(cores)
     except Exception:  # pragma: no cover
-        cores = 1
+        pass
     H, Hkv, N, d, G, nb = (cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim,
                            cfg.num_proxies, cfg.nb)
     f64 = lambda a: bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
     scale = cfg.scale
     est = {}
     t_all = time.perf_counter()
+    row_k = ((lambda h, I: budget_param) if budget_kind == "fixed" else
+             (lambda h, I: O.ratio_count(I, budget_param)))
 
-    ntok = min(N, 4096)
+    # pooling, every token of every proxy
     t = time.perf_counter()
-    O.proxy_pool(f64(x["q"][:, :ntok]), f64(x["k"][:, :ntok]), G)
-    est["pool"] = (time.perf_counter() - t) * N / ntok
+    qbar = np.zeros((G, N, d))
+    kbar = np.zeros((G, N, d))
+    for g in range(G):
+        heads, kvs = O.group_query_heads(g, H, G), O.group_kv_heads(g, H, Hkv, G)
+        qg, kg = O.proxy_pool(f64(x["q"][heads]), f64(x["k"][kvs]), 1)
+        qbar[g], kbar[g] = qg[0], kg[0]
+    est["pool"] = time.perf_counter() - t
 
-    rows = sorted({(c * nb) // 16 for c in range(1, 16)})
-    qg = f64(x["q"][: H // G])
-    kg = f64(x["k"][: max(1, Hkv // G)])
+    # proxy scores: the last row and a spread of rows of every proxy
+    rows = sorted({nb - 1} | {(c * nb) // 8 for c in range(1, 8)})
+    S_ref = np.full((G, nb, nb), -np.inf)
     t = time.perf_counter()
-    qbar0 = O.round_bf16(qg.mean(axis=0))
-    kbar0 = O.round_bf16(kg.mean(axis=0))
-    tiles = 0
-    for I in rows:
-        O.proxy_score_row(qbar0, kbar0, I, B, scale, score_stride)
-        tiles += I + 1
+    for g in range(G):
+        for I in rows:
+            S_ref[g, I, : I + 1] = O.proxy_score_row(qbar[g], kbar[g], I, B, scale, score_stride)
+    tiles = G * sum(I + 1 for I in rows)
     est["score"] = (time.perf_counter() - t) * (G * nb * (nb + 1) / 2) / tiles
-    del qg, kg
+    del qbar, kbar
 
+    # budgets: the masses of every head (threads over heads), then the cumulative
+    # mass along the group's ranking of the last row
+    k_ref = None
     if budget_kind == "dynamic":
-        q0, k0 = f64(x["q"][0]), f64(x["k"][0])
+        def masses_of(h):
+            q_h, k_h = f64(x["q"][h]), f64(x["k"][O.kv_head_of(h, H, Hkv)])
+            if last_blocks == 1:
+                return O.last_block_masses(q_h, k_h, B, scale)
+            return O.last_blocks_masses(q_h, k_h, B, scale, last_blocks)
         t = time.perf_counter()
-        if last_blocks == 1:
-            O.last_block_masses(q0, k0, B, scale)
-        else:
-            O.last_blocks_masses(q0, k0, B, scale, last_blocks)
-        est["budget"] = (time.perf_counter() - t) * H
-        del q0, k0
+        with ThreadPoolExecutor(cores) as ex:
+            masses = list(ex.map(masses_of, range(H)))
+        orders = [O.rank_blocks(S_ref[g, nb - 1], nb - 1) for g in range(G)]
+        k_ref = [O.budget_from_masses(masses[h], orders[O.group_of(h, H, G)], gamma)
+                 for h in range(H)]
+        est["budget"] = time.perf_counter() - t
     else:
         est["budget"] = 0.0
 
-    srow = np.random.default_rng(1).standard_normal(nb)
+    # selection of the sampled rows of every head (scaled by rows)
     t = time.perf_counter()
-    for I in rows:
-        O.select_row(srow, I, nb // 4)
-    est["select"] = (time.perf_counter() - t) * (G * nb) / len(rows)
+    sel = {}
+    for h in range(H):
+        for I in rows:
+            kk = row_k(h, I) if k_ref is None else k_ref[h]
+            sel[h, I] = O.select_row(S_ref[O.group_of(h, H, G), I], I, kk)
+    est["select"] = (time.perf_counter() - t) * nb / len(rows)
 
     done, spent = 0, 0.0
     heads = {}
@@ -182,16 +203,46 @@ def cpu_baseline(cfg, x, samples, n_kept, budget_s=20.0, last_blocks=1, budget_k
         if spent > budget_s * 0.5:
             break
     est["sparse"] = spent * n_kept / max(done, 1)
+
+    # the GPU's mask on the sampled rows against the oracle's chain: a block may
+    # differ only within 1e-3 relative of the oracle's score across the cut
+    rp, ci, kh_gpu = gpu_csr
+    kh_gpu = [None] * H if kh_gpu is None else kh_gpu
+    differ = gap_ok = 0
+    worst = 0.0
+    total = 0
+    for (h, I), want in sel.items():
+        got = set(ci[rp[h * nb + I]:rp[h * nb + I + 1]].tolist())
+        want = set(want.tolist())
+        total += I + 1
+        s_row = S_ref[O.group_of(h, H, G), I]
+        order = O.rank_blocks(s_row, I)
+        kk = min(int(row_k(h, I) if k_ref is None else k_ref[h]), I + 1)
+        for J in want ^ got:
+            differ += 1
+            c = kk if J in want else kk - 1
+            if 0 <= c <= I and order[c] != J:
+                gap = abs(s_row[J] - s_row[order[c]]) / max(abs(s_row[J]), abs(s_row[order[c]]))
+                if gap < 1e-3:
+                    gap_ok += 1
+                    worst = max(worst, gap)
+    mask = {"rows": rows, "heads": H, "causal_blocks": total,
+            "agreement": round(1.0 - differ / max(total, 1), 7), "blocks_differing": differ,
+            "within_gap_rule": gap_ok, "outside_gap_rule": differ - gap_ok,
+            "worst_gap_within_rule": float(worst),
+            "budgets_equal_to_oracle": None if k_ref is None else
+            int(np.sum(np.asarray(k_ref) == np.asarray(kh_gpu)))}
     return {
         "value": sum(est.values()) * 1e3, "unit": "ms", "cores": int(cores), "kind": "oracle",
-        "sample": (f"float64 NumPy oracle; pooling of {ntok} tokens, proxy scores of rows {rows} "
-                   f"of proxy 0, last-block masses of head 0, selection of {len(rows)} rows, "
-                   f"sparse attention of {done} kept tiles of the GPU mask; each part scaled to "
-                   f"the full step by its work units (tokens, causal tiles, heads, rows, kept tiles)"),
+        "sample": (f"float64 NumPy oracle on {cores} threads, reported baseline only: pooling of "
+                   f"every token and the masses of all {H} heads timed in full; proxy scores of "
+                   f"rows {rows} of every proxy, their selection, and sparse attention of {done} "
+                   f"kept tiles of the GPU mask timed on that sample and scaled to the full step "
+                   f"by causal tiles, rows and kept tiles"),
         "stage_s": {k: round(v, 3) for k, v in est.items()},
         "wall_s": round(time.perf_counter() - t_all, 2),
         "cpu_model": _cpu_model(),
-    }
+    }, mask
 
 
 def _cpu_model():
@@ -363,8 +414,9 @@ def main():
         dst.copy_(src)      # calibration: 256 MiB read + 256 MiB written
         attn(dev["q"], dev["k"], dev["v"], out=o)
         for _ in range(a.steps):
-            pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
-            pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.scores)
+            pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar, attn.qexp, attn.kexp)
+            pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.qexp, attn.kexp,
+                                   attn.scores)
             budget_stage()
             select_stage()
             pxa.pxa_sparse_prefill_ex(cfg, budget, dev["q"], dev["k"], dev["v"], attn.row_ptr, attn.col_idx, o,
@@ -397,9 +449,10 @@ def main():
     for r in range(reps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         evs[0].record(stream)
-        pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar)
+        pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], attn.qbar, attn.kbar, attn.qexp, attn.kexp)
         evs[1].record(stream)
-        pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.scores)
+        pxa.pxa_proxy_score_ex(cfg, budget, attn.qbar, attn.kbar, attn.qexp, attn.kexp,
+                               attn.scores)
         evs[2].record(stream)
         budget_stage()
         evs[3].record(stream)
@@ -492,7 +545,7 @@ def main():
     if a.score_stride > 1:
         full = dataclasses.replace(budget, score_stride=1)
         S1 = torch.empty_like(attn.scores)
-        pxa.pxa_proxy_score_ex(cfg, full, attn.qbar, attn.kbar, S1)
+        pxa.pxa_proxy_score_ex(cfg, full, attn.qbar, attn.kbar, attn.qexp, attn.kexp, S1)
         kh1 = torch.empty_like(attn.k_h)
         rp1 = torch.empty_like(attn.row_ptr)
         ci1 = torch.empty_like(attn.col_idx)
@@ -524,7 +577,7 @@ def main():
     select_bytes = G * nb * nb * 4 + H * nb * 4 * 3 + n_kept * 4
 
     # CPU oracle on a bounded sample (rank 0, one GPU)
-    cpu = None
+    cpu = mask_vs_oracle = None
     if not a.no_cpu_baseline:
         ci = attn.col_idx.cpu().numpy()
         rng = np.random.default_rng(7)
@@ -534,10 +587,13 @@ def main():
                 r = h * nb + I
                 samp.append((h, I, ci[rp[r]:rp[r + 1]].astype(np.int64)))
         log("timing the CPU oracle on a sample")
-        cpu = cpu_baseline(cfg, x, samp, n_kept, budget_s=a.cpu_budget_s,
-                           last_blocks=budget.last_blocks, budget_kind=kind,
-                           score_stride=a.score_stride)
+        cpu, mask_vs_oracle = cpu_baseline(
+            cfg, x, samp, n_kept, (rp, ci, kh if kind != "ratio" else None),
+            budget_s=a.cpu_budget_s, last_blocks=budget.last_blocks, budget_kind=kind,
+            score_stride=a.score_stride, gamma=gamma,
+            budget_param=budget.fixed_blocks if kind == "fixed" else budget.ratio)
         cpu["value"] = round(cpu["value"], 1)
+        log(f"mask vs the oracle's chain on sampled rows: {mask_vs_oracle}")
 
     res = {
         "metric": METRIC, "value": round(ms_step, 3), "unit": "ms", "n_gpus": 1,
@@ -556,6 +612,7 @@ def main():
         "estimation_pct_of_dense": round(100.0 * est_ms / dense_ms, 3),
         "kept_density": round(density, 4),
         "mask_vs_every_query_scoring": stride_cmp,
+        "mask_vs_oracle_sampled": mask_vs_oracle,
         "running_max_skip": skip_cmp,
         "k_h": kh.tolist() if kind != "ratio" else None,
         "stage_ms": {n: round(v, 4) for n, v in stage.items()},

@@ -9,6 +9,7 @@ include/pxa.h); this package only marshals torch tensors to it.
     attn = ProxyAttn(cfg)              # allocates the workspace once
     o = attn(q, k, v)                  # q [H,N,d], k/v [Hkv,N,d] bf16 on the GPU
     attn.k_h, attn.row_ptr, attn.col_idx, attn.scores   # the mask it used
+    attn.qbar, attn.qexp               # proxies: fp16 values, value * 2**-exp per block
 
 Method variants: ProxyAttn(cfg, Options.dynamic(last_blocks=4)),
 Options.fixed(blocks=64), Options.ratio_of(0.1), Options.dynamic(score_stride=2),
@@ -45,8 +46,11 @@ class ProxyAttn:
             nbytes = n * torch.empty((), dtype=dtype).element_size()
             return self.ws[off:off + nbytes].view(dtype).view(*shape)
 
-        self.qbar = view(L.qbar, G * N * d, torch.bfloat16, (G, N, d))
-        self.kbar = view(L.kbar, G * N * d, torch.bfloat16, (G, N, d))
+        # block-scaled fp16 proxies: value = qbar[g, t] * 2**-qexp[g, t // 128]
+        self.qbar = view(L.qbar, G * N * d, torch.float16, (G, N, d))
+        self.kbar = view(L.kbar, G * N * d, torch.float16, (G, N, d))
+        self.qexp = view(L.qexp, G * nb, torch.int32, (G, nb))
+        self.kexp = view(L.kexp, G * nb, torch.int32, (G, nb))
         self.scores = view(L.scores, G * nb * nb, torch.float32, (G, nb, nb))
         self.masses = view(L.masses, H * nb, torch.float32, (H, nb))
         self.k_h = view(L.k_h, H, torch.int32, (H,))

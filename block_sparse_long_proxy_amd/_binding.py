@@ -56,7 +56,7 @@ class pxa_options(ctypes.Structure):
 
 class pxa_workspace_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx",
+                ("qbar", "kbar", "qexp", "kexp", "scores", "masses", "k_h", "row_ptr", "col_idx",
                  "row_order", "budget_ws", "select_ws", "total")]
 
 
@@ -74,14 +74,14 @@ _SIGNATURES = {
     "pxa_select_workspace_bytes": (ctypes.c_size_t, [_CFG]),
     "pxa_max_col_entries": (ctypes.c_size_t, [_CFG]),
     "pxa_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "pxa_proxy_pool": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
-    "pxa_proxy_score": (ctypes.c_int, [_CFG, _P, _P, _P, _P]),
+    "pxa_proxy_pool": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P]),
+    "pxa_proxy_score": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P]),
     "pxa_budget_estimate": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_block_select": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_sparse_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pxa_dense_prefill": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P]),
     "pxa_validate_options": (ctypes.c_int, [_CFG, _OPT]),
-    "pxa_proxy_score_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P]),
+    "pxa_proxy_score_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P]),
     "pxa_sparse_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, _P, _P]),
     "pxa_prefill_batch": (ctypes.c_int, [_CFG, _OPT, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                          _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -220,7 +220,8 @@ def _stream(stream):
 
 def _dt(kind):
     import torch
-    return {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32, "u8": torch.uint8}[kind]
+    return {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32, "i32": torch.int32,
+            "u8": torch.uint8}[kind]
 
 
 def _tp(x, kind, name):
@@ -232,7 +233,7 @@ def _needs(cfg: Config, tokens: Optional[int] = None) -> dict:
     H, Hkv, G, d, nb = cfg.num_heads, cfg.num_kv_heads, cfg.num_proxies, cfg.head_dim, cfg.nb
     N = cfg.seq_len if tokens is None else tokens
     return dict(q=H * N * d, o=H * N * d, k=Hkv * N * d, v=Hkv * N * d, qbar=G * N * d,
-                kbar=G * N * d, scores=G * nb * nb, k_h=H, masses=H * nb, row_ptr=H * nb + 1,
+                kbar=G * N * d, qexp=G * nb, kexp=G * nb, scores=G * nb * nb, k_h=H, masses=H * nb, row_ptr=H * nb + 1,
                 row_order=H * nb, col_idx=H * nb * (nb + 1) // 2)
 
 
@@ -305,18 +306,21 @@ def pxa_prefill(cfg: Config, q, k, v, o, ws, ws_bytes=None, stream=None) -> None
         "pxa_prefill")
 
 
-def pxa_proxy_pool(cfg: Config, q, k, qbar, kbar, stream=None) -> None:
-    _check_sizes(cfg, q=q, k=k, qbar=qbar, kbar=kbar)
+def pxa_proxy_pool(cfg: Config, q, k, qbar, kbar, qexp, kexp, stream=None) -> None:
+    """qbar, kbar: float16 [G, N, d]; qexp, kexp: int32 [G, nb] (block exponents)."""
+    _check_sizes(cfg, q=q, k=k, qbar=qbar, kbar=kbar, qexp=qexp, kexp=kexp)
     _check(load_library().pxa_proxy_pool(
         ctypes.byref(cfg.c()), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
-        _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"), _stream(stream)), "pxa_proxy_pool")
+        _tp(qbar, "f16", "qbar"), _tp(kbar, "f16", "kbar"), _tp(qexp, "i32", "qexp"),
+        _tp(kexp, "i32", "kexp"), _stream(stream)), "pxa_proxy_pool")
 
 
-def pxa_proxy_score(cfg: Config, qbar, kbar, scores, stream=None) -> None:
-    _check_sizes(cfg, qbar=qbar, kbar=kbar, scores=scores)
+def pxa_proxy_score(cfg: Config, qbar, kbar, qexp, kexp, scores, stream=None) -> None:
+    _check_sizes(cfg, qbar=qbar, kbar=kbar, qexp=qexp, kexp=kexp, scores=scores)
     _check(load_library().pxa_proxy_score(
-        ctypes.byref(cfg.c()), _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"),
-        _tp(scores, "f32", "scores"), _stream(stream)), "pxa_proxy_score")
+        ctypes.byref(cfg.c()), _tp(qbar, "f16", "qbar"), _tp(kbar, "f16", "kbar"),
+        _tp(qexp, "i32", "qexp"), _tp(kexp, "i32", "kexp"), _tp(scores, "f32", "scores"),
+        _stream(stream)), "pxa_proxy_score")
 
 
 def pxa_budget_estimate(cfg: Config, q, k, scores, k_h, masses, ws, ws_bytes=None,
@@ -358,12 +362,13 @@ def pxa_dense_prefill(cfg: Config, q, k, v, o, stream=None) -> None:
 
 
 # ---------------------------------------------------------------- method variants
-def pxa_proxy_score_ex(cfg: Config, opts: Optional[Options], qbar, kbar, scores,
+def pxa_proxy_score_ex(cfg: Config, opts: Optional[Options], qbar, kbar, qexp, kexp, scores,
                        stream=None) -> None:
-    _check_sizes(cfg, qbar=qbar, kbar=kbar, scores=scores)
+    _check_sizes(cfg, qbar=qbar, kbar=kbar, qexp=qexp, kexp=kexp, scores=scores)
     _check(load_library().pxa_proxy_score_ex(
-        ctypes.byref(cfg.c()), _bref(opts), _tp(qbar, "bf16", "qbar"), _tp(kbar, "bf16", "kbar"),
-        _tp(scores, "f32", "scores"), _stream(stream)), "pxa_proxy_score_ex")
+        ctypes.byref(cfg.c()), _bref(opts), _tp(qbar, "f16", "qbar"), _tp(kbar, "f16", "kbar"),
+        _tp(qexp, "i32", "qexp"), _tp(kexp, "i32", "kexp"), _tp(scores, "f32", "scores"),
+        _stream(stream)), "pxa_proxy_score_ex")
 
 
 def pxa_validate_options(cfg: Config, opts: Optional[Options]) -> int:

@@ -6,6 +6,11 @@
 // Causal prefill: in the diagonal block only keys j <= i count; blocks above
 // the diagonal get -inf.
 //
+// The proxies come block-scaled (fp16 values times 2^e per proxy and 128-token
+// block, e stored beside them): the fp16 MFMA products of tile (I, J) are the
+// logits times 2^(e_I + e_J), so the tile max is multiplied by the exact
+// factor 2^-(e_I + e_J) (and the softmax scale) when it is stored.
+//
 // A partial last block (128 does not divide N) is read with its missing rows
 // replaced by copies of token N-1: every pair such a copy forms is a causal
 // pair of token N-1, so its block maxima are those of the tokens present.
@@ -48,7 +53,8 @@ constexpr int kPrioMax = 1;
 // whole-row launches carry none of that index arithmetic).
 template <int D, int STRIDE, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
-    const __bf16* __restrict__ qbar, const __bf16* __restrict__ kbar, float* __restrict__ scores,
+    const _Float16* __restrict__ qbar, const _Float16* __restrict__ kbar,
+    const int32_t* __restrict__ qexp, const int32_t* __restrict__ kexp, float* __restrict__ scores,
     int G, float scale, int W, const SeqTable t) {
   // STRIDE s: rows I0, I0-1, ..., I0-s+1 share the workgroup, each with its
   // 128/s scored queries (offsets s-1, 2s-1, ..., 127), so every wave still
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   constexpr int R = STRIDE;          // rows per workgroup
   constexpr int QC = 4 / STRIDE;     // 32-query chunks per row
   static_assert(QC * STRIDE == 4, "stride 1, 2 or 4");
-  __shared__ __attribute__((aligned(16))) __bf16 kt[kScoreBufs][kBlock * D];
+  __shared__ __attribute__((aligned(16))) _Float16 kt[kScoreBufs][kBlock * D];
   __shared__ float wm[2][R][kWaves][64];         // per-wave maxima of one 64-tile chunk
 
   // sequence of a fused batch (its workgroups are consecutive), then this
@@ -68,6 +74,8 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
   kbar += (size_t)t.tok[sid] * G * D;
   scores += (size_t)G * t.sq[sid];
   const int nb = t.blk[sid + 1] - t.blk[sid];
+  qexp += (size_t)G * t.blk[sid];
+  kexp += (size_t)G * t.blk[sid];
   const int tail = N - (nb - 1) * kBlock;        // tokens of the last block (128 unless partial)
   // Level lev of a row group covers its key tiles [lev W, lev W + W); the
   // row groups that reach level lev are the ceil((nb - lev W) / R) longest
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
 
   // chunk c serves row I0 - c / QC; the lane's query offset inside that block
   auto qoff = [&](int c) { return STRIDE * (32 * (c % QC) + (l & 31)) + STRIDE - 1; };
-  bf16x8 qf[4][D / 16];
+  f16x8 qf[4][D / 16];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int Ir = I0 - c / QC;
@@ -104,10 +112,10 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       load_qfrag<D>(qbar + ((size_t)g * N + (size_t)qt) * D, qf[c]);
     } else {
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[c][s] = bf16x8{};
+      for (int s = 0; s < D / 16; ++s) qf[c][s] = f16x8{};
     }
   }
-  const __bf16* kb = uniform_ptr(kbar + (size_t)g * N * D);
+  const _Float16* kb = uniform_ptr(kbar + (size_t)g * N * D);
   if (lev == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -118,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     }
   }
   // Threads 0..64R-1: combine chunk cc (tiles 64cc .. 64cc+63) of the four
-  // key slices, for row I0 - (thread / 64).
+  // key slices, for row I0 - (thread / 64), and undo the block scales.
   auto store_chunk = [&](int cc) {
     if (threadIdx.x < 64 * R) {
       const int r = threadIdx.x >> 6;
@@ -126,14 +134,15 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
       const int J = 64 * cc + l;
       if (Ir >= 0 && J <= Ir) {
         const float* p = &wm[cc & 1][r][0][l];
+        const int ex = qexp[(size_t)g * nb + Ir] + kexp[(size_t)g * nb + J];
         scores[((size_t)g * nb + Ir) * nb + J] =
-            fmaxf(fmaxf(p[0], p[64]), fmaxf(p[128], p[192])) * scale;
+            ldexpf(fmaxf(fmaxf(p[0], p[64]), fmaxf(p[128], p[192])), -ex) * scale;
       }
     }
   };
 
   // key tile J into buffer b; only tile nb-1 can be partial
-  auto load_tile = [&](int J, __bf16* buf) {
+  auto load_tile = [&](int J, _Float16* buf) {
     if (J == nb - 1 && tail < kBlock)
       tile_load_lds_rows<D, false>(kb + (size_t)J * kTile, buf, tail);
     else
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
     if (J + 1 <= J1) load_tile(J + 1, kt[(J + 1) % kScoreBufs]);
     if (J > J0 && (J & 63) == 0) store_chunk((J >> 6) - 1);   // written before the barrier
-    const __bf16* cur = kt[J % kScoreBufs];
+    const _Float16* cur = kt[J % kScoreBufs];
     f32x16 acc[4];
     __builtin_amdgcn_s_setprio(kPrioProducts);
 #pragma unroll
@@ -156,10 +165,10 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
     // The fragment of k-step s+1 is read before the four products of step s
     // issue (scheduling barriers keep that order; the default schedule reuses
     // one register set and waits for every read).
-    bf16x8 a = ktile_frag<D>(cur, ws, 0);
+    f16x8 a = ktile_frag<D>(cur, ws, 0);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      bf16x8 an = a;
+      f16x8 an = a;
       if (s + 1 < D / 16) an = ktile_frag<D>(cur, ws, s + 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -206,7 +215,8 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score_kernel(
 constexpr long kScoreSlots = 512;
 
 hipError_t launch_proxy_score(const LaunchArgs& a, const SeqTable& t, const void* qbar,
-                              const void* kbar, float* scores, hipStream_t stream) {
+                              const void* kbar, const int32_t* qexp, const int32_t* kexp,
+                              float* scores, hipStream_t stream) {
   // Key tiles per workgroup: whole rows when the longest row is at most half
   // the mean load of a slot (the longest-first order then balances), else
   // multiples of 64 tiles near that half, so a few long rows do not leave
@@ -232,8 +242,8 @@ hipError_t launch_proxy_score(const LaunchArgs& a, const SeqTable& t, const void
   }
   const dim3 grid(tw.swg[t.n]), block(kThreads);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const __bf16*)qbar, (const __bf16*)kbar,
-                       scores, a.G, a.scale, W, tw);
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, (const _Float16*)qbar,
+                       (const _Float16*)kbar, qexp, kexp, scores, a.G, a.scale, W, tw);
   };
   const bool split = W < nbmax;
   auto pick = [&](auto d) {

@@ -128,6 +128,8 @@ void layout_of_table(const pxa::LaunchArgs& a, const pxa::SeqTable& t, pxa_works
   };
   L->qbar = take((size_t)a.G * toks * a.D * 2);
   L->kbar = take((size_t)a.G * toks * a.D * 2);
+  L->qexp = take((size_t)a.G * blks * 4);
+  L->kexp = take((size_t)a.G * blks * 4);
   L->scores = take((size_t)a.G * sq * 4);
   L->masses = take((size_t)a.H * blks * 4);
   L->k_h = take((size_t)a.H * t.n * 4);
@@ -152,6 +154,8 @@ int run_method(const pxa::LaunchArgs& a, const pxa::SeqTable& t, const void* q, 
   char* w = (char*)ws;
   void* qbar = w + L.qbar;
   void* kbar = w + L.kbar;
+  int32_t* qexp = (int32_t*)(w + L.qexp);
+  int32_t* kexp = (int32_t*)(w + L.kexp);
   float* scores = (float*)(w + L.scores);
   float* masses = (float*)(w + L.masses);
   int32_t* k_h = (int32_t*)(w + L.k_h);
@@ -159,8 +163,8 @@ int run_method(const pxa::LaunchArgs& a, const pxa::SeqTable& t, const void* q, 
   int32_t* col_idx = (int32_t*)(w + L.col_idx);
   int32_t* row_order = (int32_t*)(w + L.row_order);
   int rc;
-  if ((rc = hip_rc(pxa::launch_proxy_pool(a, t, q, k, qbar, kbar, s)))) return rc;
-  if ((rc = hip_rc(pxa::launch_proxy_score(a, t, qbar, kbar, scores, s)))) return rc;
+  if ((rc = hip_rc(pxa::launch_proxy_pool(a, t, q, k, qbar, kbar, qexp, kexp, s)))) return rc;
+  if ((rc = hip_rc(pxa::launch_proxy_score(a, t, qbar, kbar, qexp, kexp, scores, s)))) return rc;
   if (a.budget_mode == pxa::kBudgetDynamic)
     rc = hip_rc(pxa::launch_budget(a, t, q, k, scores, k_h, masses, w + L.budget_ws, s));
   else if (a.budget_mode == pxa::kBudgetFixed)
@@ -302,27 +306,29 @@ size_t pxa_budget_workspace_bytes_ex(const pxa_config* cfg, const pxa_options* b
 }
 
 int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k, void* qbar, void* kbar,
-                   void* stream) {
+                   int32_t* qexp, int32_t* kexp, void* stream) {
   int rc = check_config(cfg);
   if (rc) return rc;
-  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {qbar, 16}, {kbar, 16}}))) return rc;
+  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {qbar, 16}, {kbar, 16}, {qexp, 4}, {kexp, 4}}))) return rc;
   const pxa::LaunchArgs a = args_of(cfg);
-  return hip_rc(pxa::launch_proxy_pool(a, pxa::one_seq(a), q, k, qbar, kbar, (hipStream_t)stream));
+  return hip_rc(pxa::launch_proxy_pool(a, pxa::one_seq(a), q, k, qbar, kbar, qexp, kexp,
+                                       (hipStream_t)stream));
 }
 
 int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const void* qbar,
-                       const void* kbar, float* scores, void* stream) {
+                       const void* kbar, const int32_t* qexp, const int32_t* kexp,
+                       float* scores, void* stream) {
   int rc = check_all(cfg, opts);
   if (rc) return rc;
-  if ((rc = ptrs_ok({{qbar, 16}, {kbar, 16}, {scores, 4}}))) return rc;
+  if ((rc = ptrs_ok({{qbar, 16}, {kbar, 16}, {qexp, 4}, {kexp, 4}, {scores, 4}}))) return rc;
   const pxa::LaunchArgs a = args_of(cfg, opts);
-  return hip_rc(pxa::launch_proxy_score(a, pxa::one_seq(a), qbar, kbar, scores,
+  return hip_rc(pxa::launch_proxy_score(a, pxa::one_seq(a), qbar, kbar, qexp, kexp, scores,
                                         (hipStream_t)stream));
 }
 
-int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar, float* scores,
-                    void* stream) {
-  return pxa_proxy_score_ex(cfg, nullptr, qbar, kbar, scores, stream);
+int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar,
+                    const int32_t* qexp, const int32_t* kexp, float* scores, void* stream) {
+  return pxa_proxy_score_ex(cfg, nullptr, qbar, kbar, qexp, kexp, scores, stream);
 }
 
 int pxa_budget_estimate_ex(const pxa_config* cfg, const pxa_options* budget, const void* q,

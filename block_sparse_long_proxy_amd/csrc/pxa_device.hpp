@@ -20,6 +20,8 @@ namespace pxa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBlock = 128;     // key/query block edge (tokens)
@@ -29,6 +31,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x16 zero16() {
@@ -47,23 +53,27 @@ __device__ __forceinline__ int ktile_off(int row, int chunk) {
   return row * D + ((chunk ^ (row & (C - 1))) << 3);
 }
 
-// A operand (keys x d) of sub-tile `t` (32 keys) and k-step `s` (16 dims).
-template <int D>
-__device__ __forceinline__ bf16x8 ktile_frag(const __bf16* lds, int t, int s) {
+// A operand (keys x d) of sub-tile `t` (32 keys) and k-step `s` (16 dims);
+// T is the 16-bit element type (bf16 inputs or fp16 proxies).
+template <int D, typename T = __bf16>
+__device__ __forceinline__ T __attribute__((ext_vector_type(8))) ktile_frag(const T* lds, int t, int s) {
+  typedef T v8 __attribute__((ext_vector_type(8)));
   const int l = threadIdx.x & 63;
   const int row = t * 32 + (l & 31);
   const int chunk = 2 * s + (l >> 5);
-  return *reinterpret_cast<const bf16x8*>(lds + ktile_off<D>(row, chunk));
+  return *reinterpret_cast<const v8*>(lds + ktile_off<D>(row, chunk));
 }
 
 // B operand (d x queries) for k-step s, read straight from global memory:
 // query row `qrow` (pointer to its first element), dims 16 s + 8 hi .. +7.
-template <int D>
-__device__ __forceinline__ void load_qfrag(const __bf16* __restrict__ qrow, bf16x8 (&qf)[D / 16]) {
+template <int D, typename T = __bf16>
+__device__ __forceinline__ void load_qfrag(const T* __restrict__ qrow,
+                                           T __attribute__((ext_vector_type(8))) (&qf)[D / 16]) {
+  typedef T v8 __attribute__((ext_vector_type(8)));
   const int hi = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hi);
+    qf[s] = *reinterpret_cast<const v8*>(qrow + 16 * s + 8 * hi);
 }
 
 // S^T (128 keys x 32 queries of this wave) = K_tile . Q^T, four 32x32 tiles.
@@ -203,8 +213,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // row only modulo NW * ROWS (a multiple of 16), which is the same for every
 // instruction of a wave, so one per-lane byte offset serves all of them and
 // only the scalar base moves.
-template <int D, bool IS_V, int NW = kWaves>
-__device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf16* lds) {
+template <int D, bool IS_V, int NW = kWaves, typename T>
+__device__ __forceinline__ void tile_load_lds(const T* __restrict__ g, T* lds) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
   constexpr int C = D / 8;                    // 16-byte chunks per row
   constexpr int ROWS = 64 / C;                // rows per wave instruction
   constexpr int INSTS = kBlock / ROWS / NW;
@@ -228,9 +239,9 @@ __device__ __forceinline__ void tile_load_lds(const __bf16* __restrict__ g, __bf
 // past them receives a copy of row rows-1, so no address beyond the tile's
 // last token is formed.  The source row now varies per instruction, so the
 // per-lane offset is recomputed each time from the unchanged scalar base.
-template <int D, bool IS_V, int NW = kWaves>
-__device__ __forceinline__ void tile_load_lds_rows(const __bf16* __restrict__ g, __bf16* lds,
-                                                   int rows) {
+template <int D, bool IS_V, int NW = kWaves, typename T>
+__device__ __forceinline__ void tile_load_lds_rows(const T* __restrict__ g, T* lds, int rows) {
+  static_assert(sizeof(T) == 2, "16-bit elements");
   constexpr int C = D / 8;
   constexpr int ROWS = 64 / C;
   constexpr int INSTS = kBlock / ROWS / NW;

@@ -67,10 +67,13 @@ inline int max_len(const SeqTable& t) {
 }
 inline int max_blocks(const SeqTable& t) { return num_blocks(max_len(t)); }
 
+// proxies: fp16 [G][N][d] per sequence, block exponents int32 [G][nb] per sequence
 hipError_t launch_proxy_pool(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,
-                             void* qbar, void* kbar, hipStream_t stream);
+                             void* qbar, void* kbar, int32_t* qexp, int32_t* kexp,
+                             hipStream_t stream);
 hipError_t launch_proxy_score(const LaunchArgs& a, const SeqTable& t, const void* qbar,
-                              const void* kbar, float* scores, hipStream_t stream);
+                              const void* kbar, const int32_t* qexp, const int32_t* kexp,
+                              float* scores, hipStream_t stream);
 // ws: budget_ws_bytes(a, t) bytes
 size_t budget_ws_bytes(const LaunchArgs& a, const SeqTable& t);
 hipError_t launch_budget(const LaunchArgs& a, const SeqTable& t, const void* q, const void* k,

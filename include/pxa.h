@@ -22,8 +22,10 @@
  *    last block is partial and every step uses the tokens it has), G proxies.
  *  - Query head h uses KV head h / (H / Hkv).  Proxy group g holds query heads
  *    [g*H/G, (g+1)*H/G) and the (contiguous) KV heads those use.
- *  - Q, O: bfloat16 [H][N][d]; K, V: bfloat16 [Hkv][N][d]; proxies Qbar, Kbar:
- *    bfloat16 [G][N][d]; all row-major and contiguous.  Tensor pointers are
+ *  - Q, O: bfloat16 [H][N][d]; K, V: bfloat16 [Hkv][N][d]; all row-major and
+ *    contiguous.  Proxies Qbar, Kbar are block-scaled fp16 [G][N][d] with
+ *    int32 exponents qexp, kexp [G][nb]: element t of block I of proxy g holds
+ *    fp16(mean * 2^exp[g][I]) (see pxa_proxy_pool).  Tensor pointers are
  *    device pointers, 16-byte aligned; int32/fp32 arrays 4-byte aligned;
  *    workspaces 256-byte aligned.
  *  - The caller owns every buffer (inputs, outputs, workspace).  The library
@@ -48,7 +50,7 @@
 extern "C" {
 #endif
 
-#define PXA_ABI_VERSION 7
+#define PXA_ABI_VERSION 8
 
 enum {
   PXA_OK = 0,
@@ -111,8 +113,10 @@ typedef struct pxa_options {
 /* Sizes and offsets of the whole-pipeline workspace (bytes from its start).
  * Intermediates are left there by pxa_prefill so a caller can inspect them. */
 typedef struct pxa_workspace_layout {
-  size_t qbar;      /* bf16 [G][N][d]                    */
-  size_t kbar;      /* bf16 [G][N][d]                    */
+  size_t qbar;      /* fp16 [G][N][d] (block-scaled)     */
+  size_t kbar;      /* fp16 [G][N][d] (block-scaled)     */
+  size_t qexp;      /* int32 [G][nb]: exponents of qbar  */
+  size_t kexp;      /* int32 [G][nb]: exponents of kbar  */
   size_t scores;    /* fp32 [G][nb][nb]                  */
   size_t masses;    /* fp32 [H][nb]                      */
   size_t k_h;       /* int32 [H]                         */
@@ -190,8 +194,8 @@ size_t pxa_batch_workspace_bytes(const pxa_config* cfg, const pxa_options* opts,
                                  int32_t num_seqs, const int32_t* seq_lens);
 /* Layout of the fused workspace of a batch that forms one group (at most
  * PXA_MAX_FUSED_SEQS sequences): every part is the concatenation of the
- * sequences' own parts in order (qbar/kbar [G][N_s][d] each, scores
- * [G][nb_s][nb_s] each, masses [H][nb_s] each, k_h [H] each, then one CSR
+ * sequences' own parts in order (qbar/kbar [G][N_s][d] each, qexp/kexp
+ * [G][nb_s] each, scores [G][nb_s][nb_s] each, masses [H][nb_s] each, k_h [H] each, then one CSR
  * over all rows -- sequence s's H*nb_s rows after those of the sequences
  * before it, column indices local to the sequence -- and one row_order over
  * those rows).  PXA_EINVAL if the batch forms more than one group. */
@@ -203,24 +207,31 @@ int pxa_prefill_batch(const pxa_config* cfg, const pxa_options* opts, int32_t nu
                       void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 1, head pooling (blog post section 4, step 1 "Head Pooling"; section 3
- * calls it a simple pooling).  qbar[g] = mean of q over the group's query
- * heads, kbar[g] = mean of k over the group's KV heads; fp32 sums, one
- * round-to-nearest-even conversion to bf16 per element. */
+ * calls it a simple pooling).  The proxy means are qbar = mean of q over the
+ * group's query heads and kbar = mean of k over the group's KV heads (fp32
+ * sums in head order, IEEE division).  They are stored block-scaled: for proxy
+ * g and block I, exp[g][I] = e is the integer that puts the block's largest
+ * |mean| in [2^14, 2^15) (0 for an all-zero block), and every element of the
+ * block is stored as fp16(mean * 2^e), rounded to nearest even.  qbar, kbar:
+ * fp16 [G][N][d] (16-byte aligned); qexp, kexp: int32 [G][nb]. */
 int pxa_proxy_pool(const pxa_config* cfg, const void* q, const void* k,
-                   void* qbar, void* kbar, void* stream);
+                   void* qbar, void* kbar, int32_t* qexp, int32_t* kexp, void* stream);
 
 /* Step 1, score estimation (section 4, step 1 "Score Estimation": token-level
  * proxy scores, block max-pool, the QK product fused with the pooling).
  * scores[g][I][J] = scale * max over causal token pairs (i in block I,
  * j in block J, j <= i) of qbar[g][i] . kbar[g][j], fp32, for J <= I; -inf
- * for J > I.  bf16 MFMA products, fp32 accumulation. */
+ * for J > I, where qbar, kbar are the proxy values of pxa_proxy_pool (the
+ * stored fp16 times 2^-exp).  fp16 MFMA products, fp32 accumulation; the
+ * tile max is multiplied by 2^-(qexp[g][I] + kexp[g][J]) and the scale. */
 int pxa_proxy_score(const pxa_config* cfg, const void* qbar, const void* kbar,
-                    float* scores, void* stream);
+                    const int32_t* qexp, const int32_t* kexp, float* scores, void* stream);
 /* The same with the sequence-level skip: opts->score_stride = s scores only
  * the queries at offsets s-1, 2s-1, ..., B-1 of each query block (every key
  * of the causal range); s = 1 (or NULL opts) is pxa_proxy_score. */
 int pxa_proxy_score_ex(const pxa_config* cfg, const pxa_options* opts, const void* qbar,
-                       const void* kbar, float* scores, void* stream);
+                       const void* kbar, const int32_t* qexp, const int32_t* kexp,
+                       float* scores, void* stream);
 
 /* Step 2, dynamic budget (section 4, step 2: the last query block estimates
  * each head's block-level sparsity; the abstract's "block-aware dynamic budget

@@ -33,12 +33,12 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
         assert n in B._SIGNATURES, n
-    assert pxa.pxa_abi_version() == 7
+    assert pxa.pxa_abi_version() == 8
 
 
 def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.pxa_config) == 32
-    assert ctypes.sizeof(B.pxa_workspace_layout) == 11 * ctypes.sizeof(ctypes.c_size_t)
+    assert ctypes.sizeof(B.pxa_workspace_layout) == 13 * ctypes.sizeof(ctypes.c_size_t)
     assert ctypes.sizeof(B.pxa_options) == 24
     with open(os.path.join(ROOT, "include", "pxa.h")) as f:
         hdr = f.read()
@@ -107,10 +107,12 @@ def test_budget_workspace_sizes():
 def test_score_entry_point_validates_stride_before_launch():
     cfg = _good()
     _expect(B.PXA_EINVAL, pxa.pxa_proxy_score_ex, cfg, pxa.Options.dynamic(score_stride=3),
-            A, A, A, stream=0)
+            A, A, A, A, A, stream=0)
     _expect(B.PXA_ENULL, pxa.pxa_proxy_score_ex, cfg, pxa.Options.dynamic(score_stride=2),
-            A, None, A, stream=0)
-    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score_ex, cfg, None, MIS, A, A, stream=0)
+            A, None, A, A, A, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_proxy_score_ex, cfg, None, A, A, A, None, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score_ex, cfg, None, MIS, A, A, A, A, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score_ex, cfg, None, A, A, A + 2, A, A, stream=0)
 
 
 def test_attention_entry_points_validate_options_before_launch():
@@ -228,7 +230,8 @@ def test_workspace_layout_is_ordered_aligned_and_sized():
     cfg = _good()
     L = pxa.pxa_get_workspace_layout(cfg)
     H, G, N, d, nb = 8, 2, 1024, 128, 8
-    parts = [("qbar", G * N * d * 2), ("kbar", G * N * d * 2), ("scores", G * nb * nb * 4),
+    parts = [("qbar", G * N * d * 2), ("kbar", G * N * d * 2), ("qexp", G * nb * 4),
+             ("kexp", G * nb * 4), ("scores", G * nb * nb * 4),
              ("masses", H * nb * 4), ("k_h", H * 4), ("row_ptr", (H * nb + 1) * 4),
              ("col_idx", H * nb * (nb + 1) // 2 * 4), ("row_order", H * nb * 4),
              ("budget_ws", pxa.pxa_budget_workspace_bytes(cfg)),
@@ -252,8 +255,8 @@ def _expect(code, fn, *args, **kw):
 
 def test_compute_entry_points_reject_bad_config_before_launch():
     bad = _good(num_heads=7)
-    _expect(B.PXA_EINVAL, pxa.pxa_proxy_pool, bad, A, A, A, A, stream=0)
-    _expect(B.PXA_EINVAL, pxa.pxa_proxy_score, bad, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_proxy_pool, bad, A, A, A, A, A, A, stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_proxy_score, bad, A, A, A, A, A, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_budget_estimate, bad, A, A, A, A, A, A, ws_bytes=1 << 30, stream=0)
     _expect(B.PXA_EINVAL, pxa.pxa_block_select, bad, A, A, A, A, A, ws_bytes=1 << 30, stream=0,
             row_order=A)
@@ -266,8 +269,10 @@ def test_null_and_misaligned_pointers():
     cfg = _good()
     _expect(B.PXA_ENULL, pxa.pxa_dense_prefill, cfg, A, A, 0, A, stream=0)
     _expect(B.PXA_EALIGN, pxa.pxa_dense_prefill, cfg, A, MIS, A, A, stream=0)
-    _expect(B.PXA_ENULL, pxa.pxa_proxy_pool, cfg, A, A, A, 0, stream=0)
-    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score, cfg, A, A, A + 2, stream=0)      # fp32 needs 4
+    _expect(B.PXA_ENULL, pxa.pxa_proxy_pool, cfg, A, A, A, 0, A, A, stream=0)
+    _expect(B.PXA_ENULL, pxa.pxa_proxy_pool, cfg, A, A, A, A, A, 0, stream=0)
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_pool, cfg, A, A, A, A, A + 2, A, stream=0)   # int32 needs 4
+    _expect(B.PXA_EALIGN, pxa.pxa_proxy_score, cfg, A, A, A, A, A + 2, stream=0)      # fp32 needs 4
     _expect(B.PXA_EALIGN, pxa.pxa_block_select, cfg, A, A, A, A, A + 64, ws_bytes=1 << 30, stream=0)
     _expect(B.PXA_ENULL, pxa.pxa_sparse_prefill, cfg, A, A, A, A, 0, A, stream=0)
     _expect(B.PXA_EALIGN, pxa.pxa_sparse_prefill, cfg, A, A, A, A, A, A, stream=0, row_order=A + 2)
@@ -310,6 +315,8 @@ def test_binding_refuses_tensors_smaller_than_the_configuration():
     H, Hkv, N, d, G, nb = (cfg.num_heads, cfg.num_kv_heads, cfg.seq_len, cfg.head_dim,
                            cfg.num_proxies, cfg.nb)
     bf = lambda n: torch.zeros(n, dtype=torch.bfloat16)  # noqa: E731
+    hf = lambda n: torch.zeros(n, dtype=torch.float16)  # noqa: E731
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)  # noqa: E731
     q, kv = bf(H * N * d), bf(Hkv * N * d)
     with pytest.raises(ValueError, match="^q: "):
         pxa.pxa_dense_prefill(cfg, bf(H * N * d - 1), kv, kv, q, stream=0)
@@ -317,8 +324,11 @@ def test_binding_refuses_tensors_smaller_than_the_configuration():
         pxa.pxa_sparse_prefill(cfg, q, kv, bf(Hkv * (N - 128) * d), torch.zeros(H * nb + 1, dtype=torch.int32),
                                torch.zeros(1, dtype=torch.int32), q, stream=0)
     with pytest.raises(ValueError, match="^scores: "):
-        pxa.pxa_proxy_score(cfg, bf(G * N * d), bf(G * N * d),
+        pxa.pxa_proxy_score(cfg, hf(G * N * d), hf(G * N * d), i32(G * nb), i32(G * nb),
                             torch.zeros(G * nb * nb - 1, dtype=torch.float32), stream=0)
+    with pytest.raises(ValueError, match="^kexp: "):
+        pxa.pxa_proxy_pool(cfg, q, kv, hf(G * N * d), hf(G * N * d), i32(G * nb), i32(G * nb - 1),
+                           stream=0)
     with pytest.raises(ValueError, match="^col_idx: "):
         pxa.pxa_block_select(cfg, torch.zeros(G * nb * nb), torch.zeros(H, dtype=torch.int32),
                              torch.zeros(H * nb + 1, dtype=torch.int32),
@@ -350,7 +360,8 @@ def test_partial_last_block_sizes():
     assert cfg.nb == 8
     H, G, N, d, nb = 8, 2, 1000, 128, 8
     L = pxa.pxa_get_workspace_layout(cfg)
-    assert L.kbar - L.qbar >= G * N * d * 2 and L.scores - L.kbar >= G * N * d * 2
+    assert L.kbar - L.qbar >= G * N * d * 2 and L.qexp - L.kbar >= G * N * d * 2
+    assert L.kexp - L.qexp >= G * nb * 4 and L.scores - L.kexp >= G * nb * 4
     assert L.masses - L.scores >= G * nb * nb * 4
     assert pxa.pxa_max_col_entries(cfg) == H * nb * (nb + 1) // 2
     assert pxa.pxa_budget_workspace_bytes(cfg) >= H * nb * 128 * 4
@@ -366,8 +377,8 @@ def _layout_sizes(H, G, d, lens, m=1):
     """Byte sizes of the fused workspace parts, summed over the sequences."""
     nbs = [-(-n // 128) for n in lens]
     toks, blks = sum(lens), sum(nbs)
-    return {"qbar": G * toks * d * 2, "kbar": G * toks * d * 2,
-            "scores": G * sum(nb * nb for nb in nbs) * 4, "masses": H * blks * 4,
+    return {"qbar": G * toks * d * 2, "kbar": G * toks * d * 2, "qexp": G * blks * 4,
+            "kexp": G * blks * 4, "scores": G * sum(nb * nb for nb in nbs) * 4, "masses": H * blks * 4,
             "k_h": H * len(lens) * 4, "row_ptr": (H * blks + 1) * 4,
             "col_idx": H * sum(nb * (nb + 1) // 2 for nb in nbs) * 4,
             "row_order": H * blks * 4, "budget_ws": H * m * blks * 128 * 4,
@@ -389,7 +400,7 @@ def test_batch_workspace_layout_concatenates_the_sequences():
     cfg = _good()                                   # H 8, G 2, d 128, seq_len 1024
     L = pxa.pxa_get_batch_workspace_layout(cfg, None, lens)
     sizes = _layout_sizes(8, 2, 128, lens)
-    order = ["qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx", "row_order",
+    order = ["qbar", "kbar", "qexp", "kexp", "scores", "masses", "k_h", "row_ptr", "col_idx", "row_order",
              "budget_ws", "select_ws"]
     prev_end = 0
     for name in order:

@@ -114,6 +114,8 @@ def test_fused_batch_intermediates_are_each_sequences_own():
         attn = pxa.ProxyAttn(pxa.Config(H, Hkv, n, d, G, 0.9))
         attn(gpu_bf16(x["q"]), gpu_bf16(x["k"]), gpu_bf16(x["v"]))
         torch.cuda.synchronize()
+        assert torch.equal(_i32(ws, L.qexp + 4 * G * blk, G * nb), attn.qexp.reshape(-1))
+        assert torch.equal(_i32(ws, L.kexp + 4 * G * blk, G * nb), attn.kexp.reshape(-1))
         assert torch.equal(_f32(ws, L.scores + 4 * G * sq, G * nb * nb), attn.scores.reshape(-1))
         assert torch.equal(_f32(ws, L.masses + 4 * H * blk, H * nb), attn.masses.reshape(-1))
         assert torch.equal(_i32(ws, L.k_h + 4 * H * s_, H), attn.k_h)

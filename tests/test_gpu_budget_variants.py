@@ -15,7 +15,7 @@ import block_sparse_long_proxy_amd as pxa  # noqa: E402
 from block_sparse_long_proxy_amd import Options  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from parity_util import (  # noqa: E402
-    host64, csr_to_keep, budget_allowed, assert_outputs_close, check_schedule, compare_masks,
+    host64, proxies64, csr_to_keep, budget_allowed, assert_outputs_close, check_schedule, compare_masks,
     MASS_ATOL, MASS_RTOL, MASK_AGREE, SCORE_RTOL)
 from test_gpu_parity import case_data, run_pool, run_score, _empty  # noqa: E402
 
@@ -38,7 +38,7 @@ def _select_ex(cfg, budget, S, kh):
 def test_probe_blocks_masses_and_budgets(name, m):
     wl, cfg, q, k, v, dev = case_data(name)
     m = min(m, cfg.nb)
-    S_dev = run_score(cfg, *run_pool(cfg, dev))
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     budget = Options.dynamic(m)
     kh = _empty((cfg.num_heads,), torch.int32)
     masses = _empty((cfg.num_heads, cfg.nb), torch.float32)
@@ -57,7 +57,7 @@ def test_probe_blocks_masses_and_budgets(name, m):
 
 def test_probe_of_one_block_equals_the_default_budget():
     wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")
-    S_dev = run_score(cfg, *run_pool(cfg, dev))
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     outs = []
     for budget in (None, Options.dynamic(1)):
         kh = _empty((cfg.num_heads,), torch.int32)
@@ -72,7 +72,7 @@ def test_probe_of_one_block_equals_the_default_budget():
 @pytest.mark.parametrize("name", NAMES)
 def test_fixed_budget_selection_exact(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    S_dev = run_score(cfg, *run_pool(cfg, dev))
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     S = host64(S_dev)
     for kk in sorted({1, 3, cfg.nb}):
         budget = Options.fixed(kk)
@@ -89,7 +89,7 @@ def test_fixed_budget_selection_exact(name):
 @pytest.mark.parametrize("name", NAMES)
 def test_ratio_selection_exact(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    S_dev = run_score(cfg, *run_pool(cfg, dev))
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     S = host64(S_dev)
     for r in (0.05, 0.3, 0.5, 1.0):
         rp, ci, order = _select_ex(cfg, Options.ratio_of(r), S_dev, None)   # k_h unused
@@ -103,7 +103,7 @@ def test_ratio_count_float32_tie():
     # 0.3 * (9+1) sits exactly half-way between two float32 values; the kernel
     # must round to nearest-even (3.0) before the ceiling, as the oracle does.
     wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")   # nb = 13 > 9
-    S_dev = run_score(cfg, *run_pool(cfg, dev))
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     rp, ci, _ = _select_ex(cfg, Options.ratio_of(0.3), S_dev, None)
     lens = np.diff(rp).reshape(cfg.num_heads, cfg.nb)
     S = host64(S_dev)
@@ -156,17 +156,18 @@ def test_prefill_ex_end_to_end(name, budget):
 @pytest.mark.parametrize("stride", [2, 4])
 def test_strided_scores_parity(name, stride):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
+    P = run_pool(cfg, dev)
     S_dev = _empty((cfg.num_proxies, cfg.nb, cfg.nb), torch.float32)
-    pxa.pxa_proxy_score_ex(cfg, Options.dynamic(score_stride=stride), qb, kb, S_dev)
+    pxa.pxa_proxy_score_ex(cfg, Options.dynamic(score_stride=stride), *P, S_dev)
     got = host64(S_dev)
-    ref = O.proxy_scores(host64(qb), host64(kb), 128, cfg.scale, query_stride=stride)
+    ref = O.proxy_scores(proxies64(P[0], P[2]), proxies64(P[1], P[3]), 128, cfg.scale,
+                         query_stride=stride)
     fin = np.isfinite(ref)
     np.testing.assert_array_equal(np.isfinite(got), fin)
     assert np.all(np.isneginf(got[~fin]))
     err = np.abs(got[fin] - ref[fin]) / np.maximum(np.abs(ref[fin]), 1.0)
     assert err.max() <= SCORE_RTOL, err.max()
-    full = host64(run_score(cfg, qb, kb))
+    full = host64(run_score(cfg, P))
     assert np.all(got[fin] <= full[fin] + 1e-6 * np.maximum(np.abs(full[fin]), 1.0))
 
 

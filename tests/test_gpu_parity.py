@@ -15,8 +15,9 @@ import block_sparse_long_proxy_amd as pxa  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from synth import CONFIGS, generate, bf16_bits_to_f32, to_bf16_bits  # noqa: E402
 from parity_util import (  # noqa: E402
-    gpu_bf16, host64, bf16_ulp_diff, csr_to_keep, compare_masks, budget_allowed,
-    assert_outputs_close, check_schedule, SCORE_RTOL, MASS_ATOL, MASS_RTOL, MASK_AGREE)
+    gpu_bf16, host64, csr_to_keep, compare_masks, budget_allowed, gpu_pool, proxies64,
+    assert_proxies_close, assert_outputs_close, check_schedule, SCORE_RTOL, MASS_ATOL, MASS_RTOL,
+    MASK_AGREE)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,15 +64,12 @@ def _empty(shape, dtype):
 
 
 def run_pool(cfg, dev):
-    G, N, d = cfg.num_proxies, cfg.seq_len, cfg.head_dim
-    qb, kb = _empty((G, N, d), torch.bfloat16), _empty((G, N, d), torch.bfloat16)
-    pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], qb, kb)
-    return qb, kb
+    return gpu_pool(cfg, dev["q"], dev["k"])
 
 
-def run_score(cfg, qb, kb):
+def run_score(cfg, P):
     S = _empty((cfg.num_proxies, cfg.nb, cfg.nb), torch.float32)
-    pxa.pxa_proxy_score(cfg, qb, kb, S)
+    pxa.pxa_proxy_score(cfg, *P, S)
     return S
 
 
@@ -95,21 +93,21 @@ def run_select(cfg, S, kh, with_order=False):
 @pytest.mark.parametrize("name", list(CASES))
 def test_pool_parity(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
-    rq, rk = O.proxy_pool(q, k, cfg.num_proxies, to_bf16=True)
-    for got, ref, what in ((qb, rq, "qbar"), (kb, rk, "kbar")):
-        ulp = bf16_ulp_diff(host64(got), ref)
-        assert ulp.max() <= 1, f"{what}: max ulp {ulp.max()}"
+    qb, kb, qe, ke = run_pool(cfg, dev)
+    rq, rk = O.proxy_pool(q, k, cfg.num_proxies)
+    for got, e, ref, what in ((qb, qe, rq, "qbar"), (kb, ke, rk, "kbar")):
+        ulp = assert_proxies_close(got.cpu().numpy(), e.cpu().numpy(), ref, what)
         if (cfg.num_heads // cfg.num_proxies) & (cfg.num_heads // cfg.num_proxies - 1) == 0:
-            assert np.mean(ulp > 0) < 1e-4, f"{what}: {np.mean(ulp > 0)} elements differ"
+            # a power-of-two member count divides exactly: only the sum rounds
+            assert np.mean(ulp > 0) < 1e-3, f"{what}: {np.mean(ulp > 0)} elements differ"
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_score_parity_on_identical_proxies(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
-    S = host64(run_score(cfg, qb, kb))
-    ref = O.proxy_scores(host64(qb), host64(kb), 128, cfg.scale)
+    P = run_pool(cfg, dev)
+    S = host64(run_score(cfg, P))
+    ref = O.proxy_scores(proxies64(P[0], P[2]), proxies64(P[1], P[3]), 128, cfg.scale)
     upper = np.triu(np.ones((cfg.nb, cfg.nb), dtype=bool), 1)
     assert np.all(np.isneginf(S[:, upper])), "blocks above the diagonal must be -inf"
     low = ~upper
@@ -121,8 +119,7 @@ def test_score_parity_on_identical_proxies(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_budget_parity_on_identical_scores(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
-    S_dev = run_score(cfg, qb, kb)
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     kh, m = run_budget(cfg, dev, S_dev)
     S = host64(S_dev)
     kh, m = kh.cpu().numpy(), m.cpu().numpy().astype(np.float64)
@@ -140,8 +137,7 @@ def test_budget_parity_on_identical_scores(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_select_parity_exact(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
-    S_dev = run_score(cfg, qb, kb)
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     kh_dev, _ = run_budget(cfg, dev, S_dev)
     rp, ci, order = run_select(cfg, S_dev, kh_dev, with_order=True)
     rp, ci, order = rp.cpu().numpy(), ci.cpu().numpy(), order.cpu().numpy()
@@ -176,8 +172,7 @@ def test_select_parity_with_planted_ties_and_budgets():
 @pytest.mark.parametrize("name", list(CASES))
 def test_sparse_attention_parity_on_gpu_mask(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = run_pool(cfg, dev)
-    S_dev = run_score(cfg, qb, kb)
+    S_dev = run_score(cfg, run_pool(cfg, dev))
     kh_dev, _ = run_budget(cfg, dev, S_dev)
     rp, ci, order = run_select(cfg, S_dev, kh_dev, with_order=True)
     o = torch.empty_like(dev["q"])

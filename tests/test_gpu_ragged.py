@@ -18,8 +18,9 @@ from block_sparse_long_proxy_amd import Options  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from synth import CONFIGS, generate, bf16_bits_to_f32, to_bf16_bits  # noqa: E402
 from parity_util import (  # noqa: E402
-    gpu_bf16, host64, bf16_ulp_diff, csr_to_keep, compare_masks, budget_allowed,
-    assert_outputs_close, check_schedule, SCORE_RTOL, MASS_ATOL, MASS_RTOL, MASK_AGREE)
+    gpu_bf16, host64, csr_to_keep, compare_masks, budget_allowed, gpu_pool, proxies64,
+    assert_proxies_close, assert_outputs_close, check_schedule, SCORE_RTOL, MASS_ATOL, MASS_RTOL,
+    MASK_AGREE)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,15 +94,13 @@ def _tail_intact(buf, cfg, sentinel=7.0):
 
 
 def _pool(cfg, dev):
-    G, N, d = cfg.num_proxies, cfg.seq_len, cfg.head_dim
-    qb, kb = _empty((G, N, d), torch.bfloat16), _empty((G, N, d), torch.bfloat16)
-    pxa.pxa_proxy_pool(cfg, dev["q"], dev["k"], qb, kb)
-    return qb, kb
+    return gpu_pool(cfg, dev["q"], dev["k"])
 
 
-def _score(cfg, qb, kb, opts=None):
+def _score(cfg, P, opts=None):
     S = _empty((cfg.num_proxies, cfg.nb, cfg.nb), torch.float32)
-    pxa.pxa_proxy_score_ex(cfg, opts, qb, kb, S)
+    qb, kb, qe, ke = P
+    pxa.pxa_proxy_score_ex(cfg, opts, qb, kb, qe, ke, S)
     return S
 
 
@@ -124,14 +123,14 @@ def _select(cfg, S, kh):
 
 def _gpu_proxies_guarded(cfg, dev):
     """Pooled proxies copied to NaN-tailed buffers (the score kernel reads them)."""
-    qb, kb = _pool(cfg, dev)
+    qb, kb, qe, ke = _pool(cfg, dev)
     tail = 128 * cfg.head_dim
     out = []
     for t in (qb, kb):
-        buf = torch.full((t.numel() + tail,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf = torch.full((t.numel() + tail,), float("nan"), dtype=torch.float16, device="cuda")
         buf[: t.numel()] = t.reshape(-1)
         out.append(buf[: t.numel()].view(t.shape))
-    return out
+    return out[0], out[1], qe, ke
 
 
 def _check_scores(S_dev, ref, nb):
@@ -148,19 +147,20 @@ def _check_scores(S_dev, ref, nb):
 @pytest.mark.parametrize("name", list(CASES))
 def test_ragged_pool_parity(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = _pool(cfg, dev)
-    rq, rk = O.proxy_pool(q, k, cfg.num_proxies, to_bf16=True)
-    for got, ref in ((qb, rq), (kb, rk)):
-        assert bf16_ulp_diff(host64(got), ref).max() <= 1
+    qb, kb, qe, ke = _pool(cfg, dev)
+    rq, rk = O.proxy_pool(q, k, cfg.num_proxies)
+    for got, e, ref, what in ((qb, qe, rq, "qbar"), (kb, ke, rk, "kbar")):
+        assert_proxies_close(got.cpu().numpy(), e.cpu().numpy(), ref, what)
 
 
 @pytest.mark.parametrize("name", list(CASES))
 @pytest.mark.parametrize("stride", [1, 2, 4])
 def test_ragged_score_parity_on_identical_proxies(name, stride):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = _gpu_proxies_guarded(cfg, dev)
-    S = _score(cfg, qb, kb, Options.dynamic(score_stride=stride))
-    ref = O.proxy_scores(host64(qb), host64(kb), 128, cfg.scale, query_stride=stride)
+    P = _gpu_proxies_guarded(cfg, dev)
+    S = _score(cfg, P, Options.dynamic(score_stride=stride))
+    ref = O.proxy_scores(proxies64(P[0], P[2]), proxies64(P[1], P[3]), 128, cfg.scale,
+                         query_stride=stride)
     _check_scores(S, ref, cfg.nb)
 
 
@@ -171,8 +171,7 @@ def test_ragged_budget_parity_on_identical_scores(name, m):
     if m > cfg.nb:
         pytest.skip("probe longer than the sequence")
     opts = Options.dynamic(last_blocks=m)
-    qb, kb = _pool(cfg, dev)
-    S_dev = _score(cfg, qb, kb)
+    S_dev = _score(cfg, _pool(cfg, dev))
     kh, masses = _budget(cfg, dev, S_dev, opts)
     S = host64(S_dev)
     kh, masses = kh.cpu().numpy(), masses.cpu().numpy().astype(np.float64)
@@ -189,8 +188,7 @@ def test_ragged_budget_parity_on_identical_scores(name, m):
 @pytest.mark.parametrize("name", list(CASES))
 def test_ragged_select_exact_and_schedule(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = _pool(cfg, dev)
-    S_dev = _score(cfg, qb, kb)
+    S_dev = _score(cfg, _pool(cfg, dev))
     kh_dev, _ = _budget(cfg, dev, S_dev)
     rp, ci, order = (t.cpu().numpy() for t in _select(cfg, S_dev, kh_dev))
     keep_ref = O.select_blocks(host64(S_dev), kh_dev.cpu().numpy(), cfg.num_heads)
@@ -202,8 +200,7 @@ def test_ragged_select_exact_and_schedule(name):
 @pytest.mark.parametrize("name", list(CASES))
 def test_ragged_sparse_attention_on_gpu_mask(name):
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = _pool(cfg, dev)
-    S_dev = _score(cfg, qb, kb)
+    S_dev = _score(cfg, _pool(cfg, dev))
     kh_dev, _ = _budget(cfg, dev, S_dev)
     rp, ci, order = _select(cfg, S_dev, kh_dev)
     buf, o = _out(cfg)
@@ -281,8 +278,7 @@ def test_ragged_skip_parity(name, lam):
     """Running-max skip on the partial last block: the short last 32-query
     group decides on the queries it has."""
     wl, cfg, q, k, v, dev = case_data(name)
-    qb, kb = _pool(cfg, dev)
-    S_dev = _score(cfg, qb, kb)
+    S_dev = _score(cfg, _pool(cfg, dev))
     kh_dev, _ = _budget(cfg, dev, S_dev)
     rp, ci, order = _select(cfg, S_dev, kh_dev)
     buf, o = _out(cfg)
@@ -374,11 +370,11 @@ def test_split_score_rows_of_a_long_sequence(stride):
     cfg = pxa.Config(4, 2, N, d, 1, wl.gamma)
     nb = cfg.nb
     dev = {n: gpu_bf16(x[n]) for n in ("q", "k")}
-    qb, kb = _pool(cfg, dev)
-    S = host64(_score(cfg, qb, kb, Options.dynamic(score_stride=stride)))
+    P = _pool(cfg, dev)
+    S = host64(_score(cfg, P, Options.dynamic(score_stride=stride)))
     tri = np.tril(np.ones((nb, nb), dtype=bool))
     assert np.all(np.isfinite(S[0][tri])) and np.all(np.isneginf(S[0][~tri]))
-    qh, kh = host64(qb)[0], host64(kb)[0]
+    qh, kh = proxies64(P[0], P[2])[0], proxies64(P[1], P[3])[0]
     for I in (0, 62, 63, 64, 65, 127, 128, 191, 250, nb - 2, nb - 1):
         ref = O.proxy_score_row(qh, kh, I, 128, cfg.scale, stride)
         err = np.abs(S[0, I, : I + 1] - ref)
