@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     pxa_budget_workspace_bytes_ex, pxa_prefill_ex, pxa_budget_estimate_ex, pxa_block_select_ex,
     pxa_sparse_prefill_ex, pxa_dense_prefill_ex, pxa_prefill_batch,
     pxa_batch_workspace_bytes, pxa_get_batch_workspace_layout,
+    pxa_prefill_noalloc, PXA_NOALLOC_SCRATCH_BYTES,
 )
 
 

@@ -90,6 +90,7 @@ _SIGNATURES = {
     "pxa_get_workspace_layout_ex": (ctypes.c_int, [_CFG, _OPT, ctypes.POINTER(pxa_workspace_layout)]),
     "pxa_budget_workspace_bytes_ex": (ctypes.c_size_t, [_CFG, _OPT]),
     "pxa_prefill_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pxa_prefill_noalloc": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P]),
     "pxa_budget_estimate_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_block_select_ex": (ctypes.c_int, [_CFG, _OPT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pxa_batch_workspace_bytes": (ctypes.c_size_t, [_CFG, _OPT, ctypes.c_int32,
@@ -398,6 +399,19 @@ def pxa_prefill_ex(cfg: Config, opts: Optional[Options], q, k, v, o, ws, ws_byte
         ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
         _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _tp(ws, "u8", "ws"), _nbytes(ws, ws_bytes),
         _stream(stream)), "pxa_prefill_ex")
+
+
+PXA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def pxa_prefill_noalloc(cfg: Config, opts: Optional[Options], q, k, v, o, stream=None) -> None:
+    """The whole method in the library's static scratch array (no workspace,
+    no allocation); configurations needing more than PXA_NOALLOC_SCRATCH_BYTES
+    raise PXA_EWORKSPACE.  Overlapping calls on one GPU race."""
+    _check_sizes(cfg, q=q, k=k, v=v, o=o)
+    _check(load_library().pxa_prefill_noalloc(
+        ctypes.byref(cfg.c()), _bref(opts), _tp(q, "bf16", "q"), _tp(k, "bf16", "k"),
+        _tp(v, "bf16", "v"), _tp(o, "bf16", "o"), _stream(stream)), "pxa_prefill_noalloc")
 
 
 def pxa_budget_estimate_ex(cfg: Config, opts: Optional[Options], q, k, scores, k_h, masses, ws,

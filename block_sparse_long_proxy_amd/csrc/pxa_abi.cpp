@@ -1,7 +1,8 @@
 // pxa_abi.cpp -- the extern "C" boundary (include/pxa.h): host-side
 // validation, workspace layout and the launch sequence.  No allocation, no
 // synchronisation, no global mutable state except a thread-local copy of the
-// last HIP error message.
+// last HIP error message and, for pxa_prefill_noalloc only, the per-device
+// address of the library's static scratch array.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -9,6 +10,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <utility>
 
 #include "../../include/pxa.h"
@@ -223,6 +225,35 @@ size_t fused_bytes(const pxa_config* cfg, const pxa_options* opts, int32_t n, co
   return need;
 }
 
+// Workspace of pxa_prefill_noalloc: one array per GPU, held from the moment
+// the library's code object is loaded on that GPU until the process ends.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in symbol): the device address comes from hipGetSymbolAddress, once
+// per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[PXA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call for that device), or the PXA_E* code of a failure.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  int rc = hip_rc(hipGetDevice(&dev));
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return PXA_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if ((rc = hip_rc(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))))) return rc;
+    if (!ptr || !aligned(ptr, 256)) return PXA_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PXA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,6 +457,20 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* budget, const void*
 int pxa_prefill(const pxa_config* cfg, const void* q, const void* k, const void* v, void* o,
                 void* ws, size_t ws_bytes, void* stream) {
   return pxa_prefill_ex(cfg, nullptr, q, k, v, o, ws, ws_bytes, stream);
+}
+
+int pxa_prefill_noalloc(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                        const void* k, const void* v, void* o, void* stream) {
+  int rc = check_all(cfg, opts);
+  if (rc) return rc;
+  pxa_workspace_layout L;
+  layout_of(cfg, opts, &L);
+  if (L.total > PXA_NOALLOC_SCRATCH_BYTES) return PXA_EWORKSPACE;   // before any HIP call
+  if ((rc = ptrs_ok({{q, 16}, {k, 16}, {v, 16}, {o, 16}}))) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  const pxa::LaunchArgs a = args_of(cfg, opts);
+  return run_method(a, pxa::one_seq(a), q, k, v, o, ws, L, (hipStream_t)stream);
 }
 
 size_t pxa_batch_workspace_bytes(const pxa_config* cfg, const pxa_options* opts,

@@ -168,6 +168,24 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q
                    const void* k, const void* v, void* o, void* ws, size_t ws_bytes,
                    void* stream);
 
+/* The whole method with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): as pxa_prefill_ex, with the workspace in
+ * a static array of PXA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates and frees
+ * nothing.  It works on the current device (the stream must belong to it); its
+ * first call on a device looks the array's address up.  PXA_EWORKSPACE, before
+ * any device work, when pxa_workspace_bytes_ex(cfg, opts) exceeds the array
+ * (64 MiB: e.g. 28,672 tokens of a 32-head, 8-KV-head, d = 128 layer with
+ * four proxies).  Every call on one GPU shares that GPU's array, and the
+ * array keeps the last call's intermediates (every one is written before it
+ * is read, so nothing needs clearing): calls that overlap in time on one GPU,
+ * on different streams or threads, race and must be serialised by the
+ * caller. */
+#define PXA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pxa_prefill_noalloc(const pxa_config* cfg, const pxa_options* opts, const void* q,
+                        const void* k, const void* v, void* o, void* stream);
+
 /* Several sequences in one call (batched / packed varlen prefill, equal or
  * different lengths).  Sequence s has seq_lens[s] tokens (host array; each in
  * [1, cfg->seq_len]); its tensors are the usual per-sequence blocks

@@ -437,3 +437,21 @@ def test_batch_workspace_invalid_inputs():
     least = min(pxa.pxa_workspace_bytes(cfg), pxa.pxa_batch_workspace_bytes(cfg, None, [256, 256]))
     _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_batch, cfg, None, [256, 256], A, A, A, A, A,
             ws_bytes=least - 256, stream=0)
+
+
+def test_noalloc_refuses_configurations_beyond_its_array_before_any_device_work():
+    """pxa_prefill_noalloc checks the workspace its configuration needs against
+    the static array (64 MiB) first, so the refusal needs no GPU."""
+    assert B.PXA_NOALLOC_SCRATCH_BYTES == 64 << 20
+    with open(os.path.join(ROOT, "include", "pxa.h")) as f:
+        assert re.search(r"#define PXA_NOALLOC_SCRATCH_BYTES \(64u << 20\)", f.read())
+    big = _good(num_heads=32, num_kv_heads=8, seq_len=32768, num_proxies=4)
+    assert pxa.pxa_workspace_bytes(big) > B.PXA_NOALLOC_SCRATCH_BYTES
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_noalloc, big, None, A, A, A, A, stream=0)
+    # a probe of many blocks grows the workspace past the array as well
+    mid = _good(num_heads=32, num_kv_heads=8, seq_len=24576, num_proxies=4)
+    assert pxa.pxa_workspace_bytes(mid) <= B.PXA_NOALLOC_SCRATCH_BYTES
+    assert pxa.pxa_workspace_bytes_ex(mid, pxa.Options.dynamic(64)) > B.PXA_NOALLOC_SCRATCH_BYTES
+    _expect(B.PXA_EWORKSPACE, pxa.pxa_prefill_noalloc, mid, pxa.Options.dynamic(64), A, A, A, A,
+            stream=0)
+    _expect(B.PXA_EINVAL, pxa.pxa_prefill_noalloc, _good(num_heads=7), None, A, A, A, A, stream=0)
