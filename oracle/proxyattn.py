@@ -17,7 +17,9 @@ it, in the order of its section 4 ("ProxyAttn方法详解"):
   budget variants             -> fixed k per head; ratio_count, select_blocks_ratio
   final sparse mask           -> select_blocks
   FlashAttention on the mask  -> sparse_attention (sparse_attention_row_skip:
-                                 BLASST's running-max skip, an approximation)
+                                 BLASST's running-max skip, an approximation;
+                                 skip_error_bound: how far any such skip can
+                                 move the output)
 
 Readings taken where the pages leave a step open (each is stated again in the
 function that applies it):
@@ -352,56 +354,94 @@ def sparse_attention_row(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
 
 def sparse_attention_row_skip(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
                               blocks: Sequence[int], I: int, block: int, scale: float,
-                              threshold: float, group: int = 32):
+                              threshold: float):
     """Output rows of query block I with BLASST's running-max skip.
 
-    BLASST (the translated BLASST paper, introduction and method): blocks are
-    processed in sequence with a running maximum of the attention scores; a
-    block whose local maximum lies so far below the running maximum that its
-    normalised weights are negligible is skipped (no exponentials, no P.V).
-    Readings: the kept blocks are visited in descending order (the diagonal
-    block first, as the GPU kernel visits them); the threshold lam in (0, 1]
-    applies to the weight ratio, so a block is skipped when
-    exp(local max - running max) < lam (scaled logits); the decision is taken
-    for `group` consecutive queries together (all of them must satisfy it);
-    a skipped block leaves the running state untouched.
+    BLASST (the translated BLASST paper, section 1 introduction and section
+    3.1): while FlashAttention processes key blocks one after another, a
+    running maximum of the attention scores is kept; a block whose local
+    maximum lies so far below the running maximum that its normalised weights
+    are negligible is skipped -- no exponentials, no value load, no P.V -- at
+    the cost of one comparison per block.  Readings where the page is open:
+    the decision is taken per query row (each row has its own running maximum
+    and its own local maximum of the block, over its causal keys); the kept
+    blocks are visited in ascending order, as FlashAttention walks the key
+    blocks; the threshold lam in (0, 1] bounds the weight ratio, so a row
+    skips a block when exp(local max - running max) < lam (scaled logits; the
+    page's calibration lam = a / L only makes sense for a ratio).  A skipped
+    block leaves the row's running state untouched; the first block a row
+    sees is never skipped.
 
-    A partial last block (r < B queries) has ceil(r / group) groups, the last
-    one short; keys past the sequence end do not exist.
+    A partial last block (r < B queries) has r rows; keys past the sequence
+    end do not exist.
 
-    Returns (out [B or r, d] float64, skipped: list of (block J, group index)).
+    Returns (out [B or r, d] float64, skipped: list of (block J, row offset)).
     """
     N = q_h.shape[0]
     qi = block_tokens(I, block, N)
-    nq = qi.size
     q64 = np.asarray(q_h[qi], dtype=np.float64)
     k64 = np.asarray(k_kv, dtype=np.float64)
     v64 = np.asarray(v_kv, dtype=np.float64)
     d = v64.shape[1]
-    m = np.full(nq, NEG_INF)
-    lsum = np.zeros(nq)
-    acc = np.zeros((nq, d))
-    skipped = []
     log_thr = math.log(threshold)
-    for J in sorted((int(b) for b in blocks if 0 <= b <= I), reverse=True):
-        cols = block_tokens(J, block, N)
-        L = scale * (q64 @ k64[cols].T)
-        L = np.where(cols[None, :] <= qi[:, None], L, NEG_INF)
-        tmax = L.max(axis=1)
-        for gi in range(-(-nq // group)):
-            rows = slice(gi * group, min((gi + 1) * group, nq))
-            mg, tg = m[rows], tmax[rows]
-            if np.all(np.isfinite(mg)) and np.all(tg - mg < log_thr):
-                skipped.append((J, gi))
+    out = np.zeros((qi.size, d))
+    skipped = []
+    for r, i in enumerate(qi):                         # one query row at a time
+        m, lsum, acc = NEG_INF, 0.0, np.zeros(d)
+        for J in sorted(int(b) for b in blocks if 0 <= b <= I):
+            cols = block_tokens(J, block, N)
+            cols = cols[cols <= i]                     # causal keys of this row
+            if cols.size == 0:
                 continue
-            m_new = np.maximum(mg, tg)
-            alpha = np.where(np.isfinite(mg), np.exp(mg - m_new), 0.0)
-            P = np.exp(L[rows] - m_new[:, None])
-            lsum[rows] = lsum[rows] * alpha + P.sum(axis=1)
-            acc[rows] = acc[rows] * alpha[:, None] + P @ v64[cols]
-            m[rows] = m_new
-    out = np.where(lsum[:, None] > 0, acc / np.where(lsum > 0, lsum, 1.0)[:, None], 0.0)
+            x = scale * (k64[cols] @ q64[r])
+            local = x.max()
+            if np.isfinite(m) and local - m < log_thr:
+                skipped.append((J, r))
+                continue
+            m_new = max(m, local)
+            alpha = math.exp(m - m_new) if np.isfinite(m) else 0.0
+            p = np.exp(x - m_new)
+            lsum = lsum * alpha + p.sum()
+            acc = acc * alpha + p @ v64[cols]
+            m = m_new
+        out[r] = acc / lsum if lsum > 0 else 0.0
     return out, skipped
+
+
+def skip_error_bound(q_h: np.ndarray, k_kv: np.ndarray, v_kv: np.ndarray,
+                     blocks: Sequence[int], I: int, block: int, scale: float,
+                     threshold: float) -> np.ndarray:
+    """Largest change, per output element, that any running-max skip with
+    threshold lam can make to the output rows of query block I.
+
+    Whatever the visiting order and the group of queries deciding together, a
+    running maximum never exceeds the row's final maximum M, so a block is
+    only ever skipped when exp(local max - M) < lam.  Let W be the total
+    weight exp(s - M) of the row's keys in such blocks (the weights of the
+    whole row sum to at least 1: the maximum's own weight).  Dropping weight
+    w <= W from numerator and denominator moves the output by at most
+    2 W max|v| / (1 - W) per component (max over the row's kept keys).
+    Returns [B or r, d]; inf where W >= 1.
+    """
+    N = q_h.shape[0]
+    qi = block_tokens(I, block, N)
+    q64 = np.asarray(q_h[qi], dtype=np.float64)
+    k64 = np.asarray(k_kv, dtype=np.float64)
+    v64 = np.asarray(v_kv, dtype=np.float64)
+    valid = sorted(int(b) for b in blocks if 0 <= b <= I)
+    bound = np.zeros((qi.size, v64.shape[1]))
+    for r, i in enumerate(qi):
+        per_block = []
+        for J in valid:
+            cols = block_tokens(J, block, N)
+            cols = cols[cols <= i]
+            if cols.size:
+                per_block.append((cols, scale * (k64[cols] @ q64[r])))
+        M = max(x.max() for _, x in per_block)
+        W = sum(np.exp(x - M).sum() for _, x in per_block if math.exp(x.max() - M) < threshold)
+        vmax = np.abs(np.concatenate([v64[c] for c, _ in per_block])).max(axis=0)
+        bound[r] = 2.0 * W * vmax / (1.0 - W) if W < 1.0 else np.inf
+    return bound
 
 
 def sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,

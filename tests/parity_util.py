@@ -20,7 +20,11 @@ Tolerances (written out once here):
   itself); a head whose budget differs (as allowed above) is compared with
   the oracle's selection at the GPU's budget;
 * outputs on the same mask: max abs <= 2e-2 and mean abs <= 2e-3 (bf16
-  output of an fp32-accumulated attention vs float64).
+  output of an fp32-accumulated attention vs float64);
+* the running-max skip (an approximation whose decisions depend on the
+  visiting order): the kernel's output against the exact output on the same
+  mask, within the oracle's bound on what any such skip can change plus the
+  output tolerance above.
 """
 from __future__ import annotations
 
@@ -249,3 +253,19 @@ def assert_outputs_close(o_gpu: np.ndarray, o_ref: np.ndarray, what: str):
     mx, mean = float(err.max()), float(err.mean())
     assert mx <= OUT_MAX_ABS and mean <= OUT_MEAN_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
     return mx, mean
+
+
+def assert_within_skip_bound(got, q, k, v, cfg, kv, h, I, blocks, lam, what):
+    """The kernel's skip output against the exact output on the same blocks:
+    within the oracle's bound on what any running-max skip with threshold lam
+    can change (skip_error_bound), plus the bf16 output tolerance; and the
+    oracle's own skip (per row, ascending blocks) within the same bound.
+    Returns how far the kernel's output moved from the exact one (max abs)."""
+    exact = O.sparse_attention_row(q[h], k[kv], v[kv], blocks, I, 128, cfg.scale)
+    bound = O.skip_error_bound(q[h], k[kv], v[kv], blocks, I, 128, cfg.scale, lam)
+    err = np.abs(got - exact)
+    assert np.all(err <= bound + OUT_MAX_ABS), f"{what}: {float(np.max(err - bound)):.3e} past the bound"
+    assert float(np.mean(np.maximum(err - bound, 0.0))) <= OUT_MEAN_ABS, what
+    own, _ = O.sparse_attention_row_skip(q[h], k[kv], v[kv], blocks, I, 128, cfg.scale, lam)
+    assert np.all(np.abs(own - exact) <= bound + 1e-12), what
+    return float(err.max())

@@ -16,7 +16,7 @@ from block_sparse_long_proxy_amd import Options  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from parity_util import (  # noqa: E402
     host64, proxies64, csr_to_keep, budget_allowed, assert_outputs_close, check_schedule, compare_masks,
-    MASS_ATOL, MASS_RTOL, MASK_AGREE, SCORE_RTOL)
+    assert_within_skip_bound, MASS_ATOL, MASS_RTOL, MASK_AGREE, SCORE_RTOL, OUT_MAX_ABS)
 from test_gpu_parity import case_data, run_pool, run_score, _empty  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -210,23 +210,9 @@ def test_skip_with_negligible_threshold_is_bit_identical(name):
     assert torch.equal(o0, o1)
 
 
-def _robust_skip_rows(q, k, v, cfg, kv_of, rows_blocks, lam):
-    """Oracle outputs of the rows whose skip decisions do not move when lam
-    moves by 0.1% either way (a decision on the threshold may go either way
-    in fp32 on the GPU)."""
-    out = {}
-    for (h, I), blocks in rows_blocks.items():
-        kv = kv_of(h)
-        res = [O.sparse_attention_row_skip(q[h], k[kv], v[kv], blocks, I, 128, cfg.scale, x)
-               for x in (lam * 0.999, lam, min(1.0, lam * 1.001))]
-        if res[0][1] == res[1][1] == res[2][1]:
-            out[(h, I)] = res[1]
-    return out
-
-
 @pytest.mark.parametrize("name", ["tiny_d64_2k", "d128_rope_13blk"])
 @pytest.mark.parametrize("lam", [1e-3, 0.05, 1.0])
-def test_sparse_skip_parity(name, lam):
+def test_sparse_skip_within_the_bound(name, lam):
     wl, cfg, q, k, v, dev = case_data(name)
     attn, rp, ci, order = _mask_of(cfg, dev)
     o = torch.empty_like(dev["q"])
@@ -236,19 +222,18 @@ def test_sparse_skip_parity(name, lam):
     H, Hkv, nb = cfg.num_heads, cfg.num_kv_heads, cfg.nb
     rp_h, ci_h, o_h = rp.cpu().numpy(), ci.cpu().numpy(), o.float().cpu().numpy().astype(np.float64)
     rng = np.random.default_rng(9)
-    rows = {(h, I): ci_h[rp_h[h * nb + I]:rp_h[h * nb + I + 1]]
-            for h in range(H) for I in sorted({nb - 1, nb // 2, *rng.integers(0, nb, 3).tolist()})}
-    ref = _robust_skip_rows(q, k, v, cfg, lambda h: O.kv_head_of(h, H, Hkv), rows, lam)
-    assert len(ref) >= 0.8 * len(rows), (len(ref), len(rows))
-    n_skipped = 0
-    for (h, I), (out, skipped) in ref.items():
-        n_skipped += len(skipped)
-        assert_outputs_close(o_h[h, I * 128:(I + 1) * 128], out, f"{name} h{h} I{I} lam {lam}")
+    moved = 0.0
+    for h in range(H):
+        for I in sorted({nb - 1, nb // 2, *rng.integers(0, nb, 3).tolist()}):
+            blocks = ci_h[rp_h[h * nb + I]:rp_h[h * nb + I + 1]]
+            moved = max(moved, assert_within_skip_bound(
+                o_h[h, I * 128:(I + 1) * 128], q, k, v, cfg, O.kv_head_of(h, H, Hkv), h, I, blocks,
+                lam, f"{name} h{h} I{I} lam {lam}"))
     if lam == 1.0:
-        assert n_skipped > 0                        # the rule did act on these inputs
+        assert moved > OUT_MAX_ABS                  # the rule did act on these inputs
 
 
-def test_dense_skip_parity():
+def test_dense_skip_within_the_bound():
     wl, cfg, q, k, v, dev = case_data("d128_rope_13blk")
     lam = 0.02
     o = torch.empty_like(dev["q"])
@@ -256,8 +241,8 @@ def test_dense_skip_parity():
     torch.cuda.synchronize()
     H, Hkv, nb = cfg.num_heads, cfg.num_kv_heads, cfg.nb
     o_h = o.float().cpu().numpy().astype(np.float64)
-    rows = {(h, I): np.arange(I + 1) for h in (0, 3, 6) for I in (nb - 1, nb // 2, 1)}
-    ref = _robust_skip_rows(q, k, v, cfg, lambda h: O.kv_head_of(h, H, Hkv), rows, lam)
-    assert len(ref) >= 0.8 * len(rows)
-    for (h, I), (out, skipped) in ref.items():
-        assert_outputs_close(o_h[h, I * 128:(I + 1) * 128], out, f"dense h{h} I{I}")
+    for h in (0, 3, 6):
+        for I in (nb - 1, nb // 2, 1):
+            assert_within_skip_bound(o_h[h, I * 128:(I + 1) * 128], q, k, v, cfg,
+                                     O.kv_head_of(h, H, Hkv), h, I, np.arange(I + 1), lam,
+                                     f"dense h{h} I{I}")

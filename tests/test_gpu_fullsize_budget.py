@@ -9,7 +9,8 @@ torch = pytest.importorskip("torch")
 import block_sparse_long_proxy_amd as pxa  # noqa: E402
 from oracle import proxyattn as O  # noqa: E402
 from synth import get_config, generate, bf16_bits_to_f32  # noqa: E402
-from parity_util import budget_allowed, check_schedule, MASS_ATOL, MASS_RTOL  # noqa: E402
+from parity_util import (  # noqa: E402
+    assert_within_skip_bound, budget_allowed, check_schedule, MASS_ATOL, MASS_RTOL)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(900)]
 
@@ -72,3 +73,30 @@ def test_fixed_and_ratio_masks(data, budget, count):
             want = O.select_row(S[O.group_of(h, H, G), I], I, count(I))
             np.testing.assert_array_equal(ci[rp[r]:rp[r + 1]], want)
     check_schedule(attn.row_order.cpu().numpy(), rp)
+
+
+@pytest.mark.parametrize("lam", [1e-3, 0.1])
+def test_running_max_skip_on_sampled_rows(data, lam):
+    """BLASST's running-max skip at 32K tokens, run as the benchmark runs it:
+    sampled (head, row) outputs against the exact attention on the same
+    blocks, within the oracle's bound on what any such skip can change."""
+    wl, cfg, x, dev = data
+    attn, rp, ci = _run(cfg, dev, pxa.Options.dynamic(skip_threshold=lam))
+    o = torch.empty_like(dev["q"])
+    pxa.pxa_prefill_ex(cfg, pxa.Options.dynamic(skip_threshold=lam), dev["q"], dev["k"], dev["v"], o,
+                       attn.ws)
+    torch.cuda.synchronize()
+    H, Hkv, nb = cfg.num_heads, cfg.num_kv_heads, cfg.nb
+    f64 = lambda a: bf16_bits_to_f32(a).astype(np.float64)  # noqa: E731
+    rng = np.random.default_rng(11)
+    moved = 0.0
+    for h in sorted(rng.choice(H, size=3, replace=False).tolist()):
+        kv = O.kv_head_of(h, H, Hkv)
+        q1, k1, v1 = f64(x["q"][h])[None], f64(x["k"][kv])[None], f64(x["v"][kv])[None]
+        for I in sorted({nb - 1, *rng.integers(nb // 2, nb, size=2).tolist()}):
+            got = o[h, I * 128:(I + 1) * 128].float().cpu().numpy().astype(np.float64)
+            moved = max(moved, assert_within_skip_bound(got, q1, k1, v1, cfg, 0, 0, I,
+                                                        ci[rp[h * nb + I]:rp[h * nb + I + 1]], lam,
+                                                        f"32K h{h} I{I} lam {lam}"))
+    print(f"[fullsize-budget] skip lam={lam}: largest change from the exact output {moved:.3e}",
+          flush=True)

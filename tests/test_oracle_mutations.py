@@ -53,7 +53,11 @@ MUTATIONS = {
     "attn_no_causal_mask": ("L = np.where(cols[None, :] <= qrows[:, None], L, NEG_INF)", "pass"),
     "attn_no_scale": ("L = scale * (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)",
                       "L = (qi @ np.asarray(k_kv[cols], dtype=np.float64).T)"),
-    "skip_any_query": ("np.all(tg - mg < log_thr)", "np.any(tg - mg < log_thr)"),
+    "skip_descending_order": ("        for J in sorted(int(b) for b in blocks if 0 <= b <= I):\n            cols",
+                              "        for J in sorted((int(b) for b in blocks if 0 <= b <= I), reverse=True):\n            cols"),
+    "skip_updates_running_state": ("                skipped.append((J, r))\n                continue\n",
+                                   "                skipped.append((J, r))\n"),
+    "skip_bound_undercounts_mass": ("if math.exp(x.max() - M) < threshold)", "if math.exp(x.max() - M) < threshold / 4)"),
     "density_diagonal_whole": ("keep.sum() - 0.5 * diag", "keep.sum()"),
     "blocks_floor": ("return -(-N // block)", "return max(1, N // block)"),
     "partial_block_past_the_end": ("np.arange(I * block, min((I + 1) * block, N))",

@@ -458,58 +458,118 @@ def test_strided_scores_reject_bad_stride():
 
 
 # ---------------------------------------------------------------- running-max skip (BLASST)
+def _brute_skip(q, k, v, blocks, I, B, scale, lam, order="ascending", group=1):
+    """Pure-Python online softmax with the running-max skip.  order: the order
+    the kept blocks are visited in; group: consecutive rows deciding together
+    (all must satisfy the skip condition).  Returns (out, skipped (J, first row
+    of the group))."""
+    N, d = len(q), len(q[0])
+    rows = list(range(I * B, min((I + 1) * B, N)))
+    nq = len(rows)
+    m, l = [-math.inf] * nq, [0.0] * nq
+    acc = [[0.0] * d for _ in range(nq)]
+    skipped = []
+    seq = sorted(b for b in blocks if 0 <= b <= I)
+    if order == "descending":
+        seq = seq[::-1]
+    for J in seq:
+        keys = range(J * B, min((J + 1) * B, N))
+        logits = [[(scale * math.fsum(q[i][c] * k[j][c] for c in range(d)) if j <= i else -math.inf)
+                   for j in keys] for i in rows]
+        for g0 in range(0, nq, group):
+            members = [r for r in range(g0, min(g0 + group, nq)) if max(logits[r]) > -math.inf]
+            if members and all(m[r] > -math.inf and math.exp(max(logits[r]) - m[r]) < lam
+                               for r in members):
+                skipped.append((J, g0))
+                continue
+            for r in members:
+                mn = max(m[r], max(logits[r]))
+                a = math.exp(m[r] - mn) if m[r] > -math.inf else 0.0
+                w = [math.exp(x - mn) if x > -math.inf else 0.0 for x in logits[r]]
+                l[r] = l[r] * a + math.fsum(w)
+                for c in range(d):
+                    acc[r][c] = acc[r][c] * a + math.fsum(wj * v[j][c] for wj, j in zip(w, keys))
+                m[r] = mn
+    return np.array(acc) / np.array(l)[:, None], skipped
+
+
 def test_skip_with_negligible_threshold_is_plain_attention():
     N, d, B = 64, 4, 16
     q, k, v = _rand((N, d), 70, 2.0), _rand((N, d), 71), _rand((N, d), 72)
     blocks = [0, 2, 3]
-    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, 3, B, 0.5, 1e-300, group=8)
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, 3, B, 0.5, 1e-300)
     assert skipped == []
     np.testing.assert_allclose(out, O.sparse_attention_row(q, k, v, blocks, 3, B, 0.5), rtol=1e-12, atol=1e-14)
+    assert np.all(O.skip_error_bound(q, k, v, blocks, 3, B, 0.5, 1e-300) == 0.0)
 
 
-def test_skip_bruteforce_decisions_and_output():
-    # pure-Python online softmax over descending blocks with per-group decisions
-    N, d, B, G = 48, 3, 16, 4
+def test_skip_bruteforce_per_row_in_ascending_order():
+    # per query row, kept blocks in ascending order (the BLASST page's reading)
+    N, d, B = 48, 3, 16
     q, k, v = _rand((N, d), 73, 2.5), _rand((N, d), 74, 1.5), _rand((N, d), 75)
+    q[:, 0] += 1.5
+    k[:16, 0] += 2.0                      # the first block dominates: later ones may be skipped
     I, blocks, lam, scale = 2, [0, 1, 2], 0.5, 3.0
-    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam, group=G)
-    m = [-math.inf] * B
-    l = [0.0] * B
-    acc = [[0.0] * d for _ in range(B)]
-    want_skip = []
-    for J in (2, 1, 0):
-        logits = [[(scale * sum(q[I * B + i][c] * k[J * B + j][c] for c in range(d))
-                    if J * B + j <= I * B + i else -math.inf) for j in range(B)] for i in range(B)]
-        for gi in range(B // G):
-            rows = range(gi * G, (gi + 1) * G)
-            if all(m[i] > -math.inf and math.exp(max(logits[i]) - m[i]) < lam for i in rows):
-                want_skip.append((J, gi))
-                continue
-            for i in rows:
-                mn = max(m[i], max(logits[i]))
-                a = math.exp(m[i] - mn) if m[i] > -math.inf else 0.0
-                w = [math.exp(x - mn) if x > -math.inf else 0.0 for x in logits[i]]
-                l[i] = l[i] * a + math.fsum(w)
-                for c in range(d):
-                    acc[i][c] = acc[i][c] * a + math.fsum(w[j] * v[J * B + j][c] for j in range(B))
-                m[i] = mn
-    assert skipped == want_skip and len(want_skip) > 0
-    np.testing.assert_allclose(out, np.array(acc) / np.array(l)[:, None], rtol=1e-12, atol=1e-14)
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam)
+    want, want_skip = _brute_skip(q, k, v, blocks, I, B, scale, lam)
+    assert sorted(skipped) == sorted(want_skip) and len(want_skip) > 0
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+    # visiting the blocks in descending order decides differently on this input
+    _, desc_skip = _brute_skip(q, k, v, blocks, I, B, scale, lam, order="descending")
+    assert sorted(desc_skip) != sorted(want_skip)
 
 
-def test_skip_set_grows_with_threshold_and_error_is_bounded():
+def test_skip_set_grows_with_threshold():
+    # a skipped block's local maximum lies below the running maximum, so the
+    # running maxima (hence every decision's left side) do not depend on lam
     N, d, B = 128, 8, 16
     q, k, v = _rand((N, d), 76, 3.0), _rand((N, d), 77, 1.5), _rand((N, d), 78)
     I, blocks = 7, list(range(8))
-    exact = O.sparse_attention_row(q, k, v, blocks, I, B, 0.5)
     prev = set()
-    for lam in (1e-6, 1e-4, 1e-2, 1e-1):
-        out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, 0.5, lam, group=4)
+    for lam in (1e-6, 1e-4, 1e-2, 1e-1, 0.5):
+        _, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, 0.5, lam)
         assert prev <= set(skipped)
         prev = set(skipped)
-        # a skipped block holds at most 16 keys of weight < lam * max weight each
-        assert np.max(np.abs(out - exact)) <= 2 * 16 * len(blocks) * lam * np.abs(v).max() + 1e-12
-    assert prev                                             # something was skipped at 0.1
+    assert prev                                             # something was skipped
+
+
+@pytest.mark.parametrize("order,group", [("ascending", 1), ("descending", 1), ("descending", 4),
+                                         ("ascending", 8)])
+def test_skip_error_bound_holds_for_any_visiting_rule(order, group):
+    """skip_error_bound bounds the change of every rule that skips on the
+    running maximum, whatever its order and decision group."""
+    N, d, B = 96, 4, 16
+    q, k, v = _rand((N, d), 79, 2.0), _rand((N, d), 80, 1.5), _rand((N, d), 81)
+    q[:, 1] += 1.0
+    k[80:, 1] += 2.5                      # keys of the diagonal block stand out
+    I, blocks, scale = 5, [0, 1, 3, 4, 5], 0.8
+    exact = O.sparse_attention_row(q, k, v, blocks, I, B, scale)
+    for lam in (1e-3, 1e-2, 0.1, 0.3):
+        out, skipped = _brute_skip(q, k, v, blocks, I, B, scale, lam, order, group)
+        bound = O.skip_error_bound(q, k, v, blocks, I, B, scale, lam)
+        assert np.all(np.abs(out - exact) <= bound + 1e-12), (lam, order, group)
+    # the largest threshold skips something (eight rows in ascending order never agree here)
+    assert skipped or (order == "ascending" and group > 1)
+
+
+def test_skip_error_bound_bruteforce_mass():
+    # W from its definition: weights of the keys in blocks whose local max is
+    # below lam times the row's final max weight, with vmax over the kept keys
+    N, d, B = 32, 2, 8
+    q, k, v = _rand((N, d), 82, 2.0), _rand((N, d), 83, 2.0), _rand((N, d), 84)
+    I, blocks, lam, scale = 3, [0, 2, 3], 0.2, 1.0
+    got = O.skip_error_bound(q, k, v, blocks, I, B, scale, lam)
+    for r, i in enumerate(range(I * B, (I + 1) * B)):
+        lg = {J: [scale * math.fsum(q[i][c] * k[j][c] for c in range(d))
+                  for j in range(J * B, (J + 1) * B) if j <= i] for J in blocks}
+        lg = {J: x for J, x in lg.items() if x}
+        M = max(max(x) for x in lg.values())
+        W = math.fsum(math.exp(y - M) for x in lg.values() if math.exp(max(x) - M) < lam for y in x)
+        keys = [j for J in lg for j in range(J * B, J * B + len(lg[J]))]
+        for c in range(d):
+            vmax = max(abs(v[j][c]) for j in keys)
+            want = 2 * W * vmax / (1 - W) if W < 1 else math.inf
+            assert math.isclose(got[r, c], want, rel_tol=1e-12, abs_tol=1e-15)
 
 
 # ---------------------------------------------------------------- partial last block (B does not divide N)
@@ -607,35 +667,19 @@ def test_ragged_pipeline_gamma_one_is_dense_and_prefix_rows_are_causal():
     np.testing.assert_array_equal(r["S"][:, :3, :3], t["S"])
 
 
-def test_ragged_skip_bruteforce_short_last_group():
-    # partial query block of 10 rows, groups of 4 -> groups of 4, 4 and 2 rows
-    N, d, B, Gq = 42, 3, 16, 4
+def test_ragged_skip_bruteforce_partial_block():
+    # partial query block of 10 rows: each row decides on its own causal keys
+    N, d, B = 42, 3, 16
     q, k, v = _rand((N, d), 107), _rand((N, d), 108), _rand((N, d), 109)
     q[:, 0] += 2.0
-    k[32:, 0] += 2.0              # the diagonal keys dominate, so earlier blocks can be skipped
+    k[:16, 0] += 2.0              # the first block dominates, so later ones can be skipped
     I, blocks, lam, scale = 2, [0, 1, 2], 0.5, 1.0
-    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam, group=Gq)
+    out, skipped = O.sparse_attention_row_skip(q, k, v, blocks, I, B, scale, lam)
+    want, want_skip = _brute_skip(q, k, v, blocks, I, B, scale, lam)
     nq = N - I * B
-    m, l = [-math.inf] * nq, [0.0] * nq
-    acc = [[0.0] * d for _ in range(nq)]
-    want_skip = []
-    for J in (2, 1, 0):
-        keys = range(J * B, min((J + 1) * B, N))
-        logits = [[(scale * sum(q[I * B + i][c] * k[j][c] for c in range(d)) if j <= I * B + i else -math.inf)
-                   for j in keys] for i in range(nq)]
-        for gi in range(3):
-            rows = range(gi * Gq, min((gi + 1) * Gq, nq))
-            if all(m[i] > -math.inf and math.exp(max(logits[i]) - m[i]) < lam for i in rows):
-                want_skip.append((J, gi))
-                continue
-            for i in rows:
-                mn = max(m[i], max(logits[i]))
-                a = math.exp(m[i] - mn) if m[i] > -math.inf else 0.0
-                w = [math.exp(x - mn) if x > -math.inf else 0.0 for x in logits[i]]
-                l[i] = l[i] * a + math.fsum(w)
-                for c in range(d):
-                    acc[i][c] = acc[i][c] * a + math.fsum(wj * v[j][c] for wj, j in zip(w, keys))
-                m[i] = mn
-    assert skipped == want_skip and (1, 2) in want_skip      # the short group is skipped too
+    assert sorted(skipped) == sorted(want_skip) and any(J == 2 for J, _ in want_skip)
     assert out.shape == (nq, d)
-    np.testing.assert_allclose(out, np.array(acc) / np.array(l)[:, None], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+    bound = O.skip_error_bound(q, k, v, blocks, I, B, scale, lam)
+    assert bound.shape == (nq, d)
+    assert np.all(np.abs(out - O.sparse_attention_row(q, k, v, blocks, I, B, scale)) <= bound + 1e-12)
