@@ -11,8 +11,9 @@
 //   select_count_kernel: one wave per (g, I); the rank of the diagonal block
 //     is a plain count of blocks ahead of it, so the row lengths (and hence
 //     row_ptr) are known without sorting.
-//   select_scan_kernel : exclusive scan of the H*nb lengths -> row_ptr, and
-//     the XCD-aware, longest-first schedule of the rows -> row_order.
+//   select_chunk_sum / select_rowptr / select_schedule: exclusive scan of the
+//     H*nb lengths -> row_ptr, and the XCD-aware, longest-first schedule of
+//     the rows -> row_order (one workgroup per XCD).
 // A fused batch has one CSR over the rows of all its sequences (sequence s's
 // rows follow those of the sequences before it), so the scan and the
 // schedule balance the XCDs over the whole batch.
@@ -25,7 +26,6 @@
 namespace pxa {
 
 constexpr int kEmitThreads = 256;
-constexpr int kScanThreads = 1024;
 
 // Ranked blocks row I keeps under the ratio budget r: ceil of the float32
 // product r * (I+1) (nearest-even, no contraction), within [1, I+1].  (The
@@ -68,9 +68,9 @@ __global__ __launch_bounds__(256) void select_count_kernel(const float* __restri
   }
 }
 
-// Exclusive scan of the n row lengths into row_ptr[0..n]; optionally also the
-// attention kernel's schedule row_order.  Workgroup b of a launch goes to XCD
-// b mod 8, and each XCD has its own L2, so the schedule is built per XCD:
+// row_ptr and the attention schedule row_order.  Workgroup b of an attention
+// launch goes to XCD b mod 8, and each XCD has its own L2, so the schedule is
+// built per XCD:
 //   * XCD x owns the rows whose midpoint in the cumulative work row_ptr falls
 //     in the x-th eighth.  Rows are numbered h * nb + I and the heads of one
 //     KV head are consecutive, so each XCD sees one or two KV heads and their
@@ -78,11 +78,15 @@ __global__ __launch_bounds__(256) void select_count_kernel(const float* __restri
 //   * position p of row_order is dealt to XCD p mod 8, so XCD x holds exactly
 //     cap_x = ceil-or-floor(n / 8) positions; its own rows fill them longest
 //     first, a surplus (its shortest rows) moves to XCDs with spare positions.
-// The longest-first order P comes from a counting sort by length (rows of
-// equal length in no fixed order) into tmp[n]; stable ranks along P per XCD
-// come from a block-wide scan of eight counters.  One workgroup; hist needs
-// max_len + 1 ints of dynamic LDS.
+// Three launches: per-chunk sums of the lengths; the exclusive scan into
+// row_ptr, which also records where each XCD's (contiguous) range of rows
+// starts; one workgroup per XCD counting-sorts its rows by length (rows of
+// equal length in no fixed order) and writes their positions.
 constexpr int kXcds = 8;
+constexpr int kScanWG = 256;                   // threads of the scan launches
+constexpr int kRowsPerThread = 16;
+constexpr int kChunkRows = kScanWG * kRowsPerThread;
+constexpr int kSchedThreads = 1024;
 
 __device__ __forceinline__ int xcd_of_row(int64_t start, int len, int64_t total) {
   // midpoint (start + len/2) scaled to [0, 8)
@@ -90,154 +94,165 @@ __device__ __forceinline__ int xcd_of_row(int64_t start, int len, int64_t total)
   return (int)min<int64_t>(x, kXcds - 1);
 }
 
-// f(i, counts[i]) for i in [a, b) in order, the loads issued eight at a time
-// (one at a time, these loops wait out a memory latency per row).
-template <typename F>
-__device__ __forceinline__ void for_counts(const int32_t* __restrict__ counts, int a, int b,
-                                           F&& f) {
-  int i = a;
-  for (; i + 8 <= b; i += 8) {
-    int c[8];
+// Sum over the workgroup (kScanWG threads); every thread gets the result.
+__device__ __forceinline__ int block_sum(int v, int* sh) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) c[u] = counts[i + u];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) f(i + u, c[u]);
-  }
-  for (; i < b; ++i) f(i, counts[i]);
-}
-
-// f(r, counts[r], row_ptr[r]) for the rows r = tmp[p], p in [a, b), in order,
-// with the loads batched the same way.
-template <typename F>
-__device__ __forceinline__ void for_order(const int32_t* __restrict__ tmp,
-                                          const int32_t* __restrict__ counts,
-                                          const int32_t* __restrict__ row_ptr, int a, int b,
-                                          F&& f) {
-  int p = a;
-  for (; p + 8 <= b; p += 8) {
-    int r[8], c[8], s[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) r[u] = tmp[p + u];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      c[u] = counts[r[u]];
-      s[u] = row_ptr[r[u]];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) f(r[u], c[u], s[u]);
-  }
-  for (; p < b; ++p) {
-    const int r = tmp[p];
-    f(r, counts[r], row_ptr[r]);
-  }
-}
-
-// Inclusive Hillis-Steele scan of part[0..kScanThreads) in place.
-__device__ __forceinline__ void block_scan(int* part) {
-  const int t = threadIdx.x;
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int x = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += x;
-    __syncthreads();
-  }
-}
-
-__global__ __launch_bounds__(kScanThreads) void select_scan_kernel(const int32_t* __restrict__ counts,
-                                                                   int32_t* __restrict__ row_ptr,
-                                                                   int32_t* __restrict__ row_order,
-                                                                   int32_t* __restrict__ tmp,
-                                                                   int n, int max_len) {
-  __shared__ int part[kScanThreads];
-  __shared__ int xc[kScanThreads][kXcds];   // per-thread counts, then exclusive prefixes
-  __shared__ int xtot[kXcds];
-  extern __shared__ int hist[];   // [max_len + 1]
-  const int t = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int a = min(n, t * per), b = min(n, a + per);
-  int s = 0;
-  for_counts(counts, a, b, [&](int, int c) { s += c; });
-  part[t] = s;
-  if (row_order)
-    for (int c = t; c <= max_len; c += kScanThreads) hist[c] = 0;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();                              // sh may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  block_scan(part);
-  int run = part[t] - s;
-  for_counts(counts, a, b, [&](int i, int c) {
-    row_ptr[i] = run;
-    run += c;
-  });
-  if (t == kScanThreads - 1) row_ptr[n] = part[t];
-  if (!row_order) return;
-  const int64_t total = part[kScanThreads - 1];
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kScanWG / 64; ++w) t += sh[w];
+  return t;
+}
 
-  // P = rows longest first (counting sort)
-  for_counts(counts, a, b, [&](int, int c) { atomicAdd(&hist[min(c, max_len)], 1); });
-  __syncthreads();   // hist complete; every read of part above is done
-  {   // bucket starts, longest bucket first: exclusive scan of hist taken from c = max_len down
+// Exclusive prefix of v over the workgroup's threads (kScanWG of them).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* sh) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (l >= o) incl += y;
+  }
+  __syncthreads();
+  if (l == 63) sh[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += sh[i];
+  return base + incl - v;
+}
+
+// Launch 1: part[c] = sum of the lengths of chunk c (kChunkRows rows).
+__global__ __launch_bounds__(kScanWG) void select_chunk_sum_kernel(const int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ part, int n) {
+  __shared__ int sh[kScanWG / 64];
+  const int a = blockIdx.x * kChunkRows + threadIdx.x * kRowsPerThread;
+  int v[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) v[k] = a + k < n ? counts[a + k] : 0;
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) s += v[k];
+  s = block_sum(s, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
+// Launch 2: row_ptr (exclusive scan of the lengths, row_ptr[n] = total) and,
+// with `bound`, bound[x] = the first row whose owner XCD is >= x (bound[8] = n).
+__global__ __launch_bounds__(kScanWG) void select_rowptr_kernel(const int32_t* __restrict__ counts,
+                                                                const int32_t* __restrict__ part,
+                                                                int32_t* __restrict__ row_ptr,
+                                                                int32_t* __restrict__ bound, int n,
+                                                                int nchunks) {
+  __shared__ int sh[kScanWG / 64];
+  const int c = blockIdx.x;
+  int off = 0, tot = 0;
+  for (int i = threadIdx.x; i < nchunks; i += kScanWG) {
+    const int p = part[i];
+    tot += p;
+    off += i < c ? p : 0;
+  }
+  off = block_sum(off, sh);
+  tot = block_sum(tot, sh);
+  const int a = c * kChunkRows + threadIdx.x * kRowsPerThread;
+  int v[kRowsPerThread];
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) v[k] = a + k < n ? counts[a + k] : 0;
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) s += v[k];
+  int run = off + block_exclusive_scan(s, sh);
+  // owner XCD of the row before this thread's first row (-1 before row 0)
+  int prev_owner = -1;
+  if (bound && a > 0 && a < n) {
+    const int len = counts[a - 1];
+    prev_owner = xcd_of_row(run - len, len, tot);
+  }
+#pragma unroll
+  for (int k = 0; k < kRowsPerThread; ++k) {
+    const int r = a + k;
+    if (r >= n) break;
+    row_ptr[r] = run;
+    if (bound) {
+      const int owner = xcd_of_row(run, v[k], tot);
+      for (int x = prev_owner + 1; x <= owner; ++x) bound[x] = r;
+      if (r == n - 1)
+        for (int x = owner + 1; x <= kXcds; ++x) bound[x] = n;
+      prev_owner = owner;
+    }
+    run += v[k];
+    if (r == n - 1) row_ptr[n] = run;
+  }
+}
+
+// Launch 3: one workgroup per XCD x.  Its rows [bound[x], bound[x+1]) get
+// ranks by a counting sort on length, longest first; rank < cap_x takes
+// position 8 rank + x, the surplus (its shortest rows) the spare positions of
+// XCDs with fewer rows than positions, in XCD order.  hist: max_len + 1 ints
+// of dynamic LDS.
+__global__ __launch_bounds__(kSchedThreads) void select_schedule_kernel(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ bound,
+    int32_t* __restrict__ row_order, int n, int max_len) {
+  extern __shared__ int hist[];                 // [max_len + 1]
+  __shared__ int lo[kXcds + 1];
+  __shared__ int part[kSchedThreads / 64];
+  const int x = blockIdx.x, t = threadIdx.x;
+  if (t <= kXcds) lo[t] = bound[t];
+  for (int c = t; c <= max_len; c += kSchedThreads) hist[c] = 0;
+  __syncthreads();
+  const int a = lo[x], b = lo[x + 1];
+  for (int r = a + t; r < b; r += kSchedThreads) atomicAdd(&hist[min(counts[r], max_len)], 1);
+  __syncthreads();
+  {   // bucket starts, longest first: exclusive scan of hist from c = max_len down
     const int nbk = max_len + 1;
-    const int per2 = (nbk + kScanThreads - 1) / kScanThreads;
-    const int q0 = min(nbk, t * per2), q1 = min(nbk, q0 + per2);
+    const int per = (nbk + kSchedThreads - 1) / kSchedThreads;
+    const int q0 = min(nbk, t * per), q1 = min(nbk, q0 + per);
     int sum = 0;
     for (int q = q0; q < q1; ++q) sum += hist[max_len - q];
-    part[t] = sum;
+    const int l = t & 63, w = t >> 6;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (l >= o) incl += y;
+    }
+    if (l == 63) part[w] = incl;
     __syncthreads();
-    block_scan(part);
-    int acc = part[t] - sum;
+    int acc = incl - sum;
+    for (int i = 0; i < w; ++i) acc += part[i];
     for (int q = q0; q < q1; ++q) {
-      const int x = hist[max_len - q];
+      const int hx = hist[max_len - q];
       hist[max_len - q] = acc;
-      acc += x;
+      acc += hx;
     }
   }
   __syncthreads();
-  for_counts(counts, a, b, [&](int i, int c) { tmp[atomicAdd(&hist[min(c, max_len)], 1)] = i; });
-  __syncthreads();   // tmp complete: the barrier's fence orders the global writes
-
-  // per-XCD ranks along P: counts of this thread's positions [a, b) of P
-  int mine[kXcds];
-#pragma unroll
-  for (int x = 0; x < kXcds; ++x) mine[x] = 0;
-  for_order(tmp, counts, row_ptr, a, b,
-            [&](int, int c, int start) { mine[xcd_of_row(start, c, total)]++; });
-#pragma unroll
-  for (int x = 0; x < kXcds; ++x) xc[t][x] = mine[x];
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {   // inclusive scan of 8 columns
-    int add[kXcds];
-#pragma unroll
-    for (int x = 0; x < kXcds; ++x) add[x] = t >= off ? xc[t - off][x] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < kXcds; ++x) xc[t][x] += add[x];
-    __syncthreads();
-  }
-  if (t < kXcds) xtot[t] = xc[kScanThreads - 1][t];
-  __syncthreads();
+  // per-XCD counts, capacities and where the surplus goes (the same in every thread)
   int cnt[kXcds], cap[kXcds], deficit_start[kXcds + 1];
+  int surplus_before = 0;
   deficit_start[0] = 0;
 #pragma unroll
-  for (int x = 0; x < kXcds; ++x) {
-    cnt[x] = xc[t][x] - mine[x];                       // ranks before this segment
-    cap[x] = n / kXcds + (x < n % kXcds ? 1 : 0);      // positions dealt to XCD x
-    deficit_start[x + 1] = deficit_start[x] + max(0, cap[x] - xtot[x]);
+  for (int y = 0; y < kXcds; ++y) {
+    cnt[y] = lo[y + 1] - lo[y];
+    cap[y] = n / kXcds + (y < n % kXcds ? 1 : 0);
+    deficit_start[y + 1] = deficit_start[y] + max(0, cap[y] - cnt[y]);
+    if (y < x) surplus_before += max(0, cnt[y] - cap[y]);
   }
-  for_order(tmp, counts, row_ptr, a, b, [&](int r, int c, int start) {
-    const int x = xcd_of_row(start, c, total);
+  for (int r = a + t; r < b; r += kSchedThreads) {
+    const int rank = atomicAdd(&hist[min(counts[r], max_len)], 1);
     int pos;
-    if (cnt[x] < cap[x]) {
-      pos = kXcds * cnt[x] + x;
-    } else {   // surplus: the sj-th surplus row along P takes the sj-th spare position
-      int sj = 0;
-#pragma unroll
-      for (int y = 0; y < kXcds; ++y) sj += max(0, cnt[y] - cap[y]);
+    if (rank < cap[x]) {
+      pos = kXcds * rank + x;
+    } else {
+      const int sj = surplus_before + rank - cap[x];
       int y = 0;
       while (y < kXcds - 1 && sj >= deficit_start[y + 1]) ++y;
-      pos = kXcds * (xtot[y] + (sj - deficit_start[y])) + y;
+      pos = kXcds * (cnt[y] + sj - deficit_start[y]) + y;
     }
-    cnt[x]++;
     row_order[pos] = r;
-  });
+  }
 }
 
 __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
@@ -312,7 +327,10 @@ __global__ __launch_bounds__(kEmitThreads) void select_emit_kernel(
   }
 }
 
-size_t select_ws_bytes(const LaunchArgs& a, const SeqTable& t) {   // row lengths + the order
+// row lengths, then the chunk sums and the XCD bounds (at most
+// ceil(rows / kChunkRows) + 9 <= rows ints when rows > kChunkRows, and fewer
+// than the part's 256-byte minimum otherwise)
+size_t select_ws_bytes(const LaunchArgs& a, const SeqTable& t) {
   return 2 * align_up((size_t)a.H * t.blk[t.n] * sizeof(int32_t), 256);
 }
 
@@ -328,11 +346,23 @@ hipError_t launch_select(const LaunchArgs& a, const SeqTable& t, const float* sc
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int max_len = nb + 1;   // a row keeps at most I + 1 <= nb blocks
-  hipLaunchKernelGGL(select_scan_kernel, dim3(1), dim3(kScanThreads),
-                     row_order ? (size_t)(max_len + 1) * sizeof(int) : 0, stream, counts, row_ptr,
-                     row_order, tmp, rows, max_len);
+  const int nchunks = (rows + kChunkRows - 1) / kChunkRows;
+  hipLaunchKernelGGL(select_chunk_sum_kernel, dim3(nchunks), dim3(kScanWG), 0, stream, counts, tmp,
+                     rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  int32_t* bound = row_order ? tmp + nchunks : nullptr;     // kXcds + 1 entries
+  hipLaunchKernelGGL(select_rowptr_kernel, dim3(nchunks), dim3(kScanWG), 0, stream, counts, tmp,
+                     row_ptr, bound, rows, nchunks);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (row_order) {
+    hipLaunchKernelGGL(select_schedule_kernel, dim3(kXcds), dim3(kSchedThreads),
+                       (size_t)(max_len + 1) * sizeof(int), stream, counts, bound, row_order, rows,
+                       max_len);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   int Pmax = 1;
   while (Pmax < nb) Pmax <<= 1;
   const size_t smem = (size_t)Pmax * 8 + align_up((size_t)nb * 2, 16);

@@ -20,6 +20,8 @@
 //   merges the partials into each query's normaliser and adds the block
 //   masses; then sorts the last row's scores in LDS (bitonic, 64-bit keys)
 //   and scans the masses in rank order (fp32, fixed chunked order) for k_h.
+#include <type_traits>
+
 #include "pxa_device.hpp"
 #include "pxa_launch.hpp"
 
@@ -64,13 +66,16 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
   };
   load(j0, ks[0]);
 
-  for (int J = j0; J < j1; ++J) {
+  // One key block; DIAG: J is the probe block itself (causal mask), which can
+  // only be the last block of this workgroup, so the mask stays out of the loop.
+  auto step = [&](int J, auto diag_c) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     wait_vmem();       // this thread's part of tile J (and the query fragments)
     __syncthreads();   // tile J visible; tile J-1's buffer is no longer read
     if (J + 1 < j1) load(J + 1, ks[(J + 1 - j0) & 1]);
     f32x16 s[4];
     tile_scores<D>(ks[(J - j0) & 1], qf, s);
-    if (J == I) {
+    if (DIAG) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -93,7 +98,10 @@ __global__ __launch_bounds__(kThreads, 2) void budget_lse_kernel(
         sum += __builtin_amdgcn_exp2f(fmaf(s[t][r], scale_log2, -mb));
     sum += __shfl_xor(sum, 32, 64);
     if (l < 32) out[(size_t)J * kBlock + qloc] = mb + log2f(sum);
-  }
+  };
+  for (int J = j0; J < j1 - 1; ++J) step(J, std::false_type{});
+  if (j1 - 1 == I) step(I, std::true_type{});
+  else step(j1 - 1, std::false_type{});
 }
 
 __device__ __forceinline__ void bitonic_sort_u64(uint64_t* keys, int P) {
