@@ -70,7 +70,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "fa_prefill_sparse_llama8b_128k_g4.md")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["block_sparse_long_proxy_amd/csrc/fa_prefill.hip",
                   "block_sparse_long_proxy_amd/csrc/pxa_device.hpp"]
 
@@ -84,12 +84,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def profiled_traffic(workload):
+def profiled_traffic(workload, config):
     """HBM bytes per sparse-attention launch from the committed rocprofv3
-    counter summary, or None if it is missing, for another workload, or taken
-    on different kernel sources."""
+    counter summary of this workload, or None if it is missing, was taken on
+    another configuration (inputs, gamma, budget, stride, skip) or on
+    different kernel sources."""
     try:
-        with open(PROFILE_SUMMARY) as f:
+        with open(os.path.join(PROFILE_DIR, f"fa_prefill_sparse_{workload}.md")) as f:
             lines = f.read().splitlines()
     except OSError:
         return None
@@ -99,6 +100,8 @@ def profiled_traffic(workload):
             k, v = line.split(":", 1)
             kv.setdefault(k.strip(), v.strip())
     if kv.get("workload") != workload or kv.get("source_sha256") != kernel_source_hash():
+        return None
+    if kv.get("config") != json.dumps(config, sort_keys=True):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -630,10 +633,11 @@ def main():
         "roofline": {"kernel": "fa_prefill_kernel<128,sparse>", "bound": "mfma",
                      "achieved": round(kept_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(kept_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": profiled_traffic(wl.name)},
+                     "traffic": None},
         "cpu_baseline": cpu,
         "host_wall_ms_per_step": round(wall_ms, 3),
     }
+    res["roofline"]["traffic"] = profiled_traffic(wl.name, res["config"])
     print(json.dumps(res), flush=True)
 
 
