@@ -55,6 +55,20 @@ def test_noalloc_with_a_method_variant():
     assert torch.equal(o_static.view(torch.int16), o_ws.view(torch.int16))
 
 
+def test_noalloc_at_the_largest_length_the_array_holds():
+    # a Llama-8B layer with four proxies: 28,883 tokens need exactly 64 MiB
+    # (a partial last block of 83 tokens), one token more does not fit
+    llama = BASE.with_(num_heads=32, num_kv_heads=8, num_proxies=4, gammas=(0.95,))
+    n = 28883
+    cfg = pxa.Config(32, 8, n, 128, 4, 0.95)
+    assert pxa.pxa_workspace_bytes(cfg) == pxa.PXA_NOALLOC_SCRATCH_BYTES
+    assert pxa.pxa_workspace_bytes(pxa.Config(32, 8, n + 1, 128, 4, 0.95)) > pxa.PXA_NOALLOC_SCRATCH_BYTES
+    x = generate(llama.with_(name="noalloc_max", seq_len=n, seed=94, n_needles=64))
+    dev = {k: gpu_bf16(x[k]) for k in ("q", "k", "v")}
+    o_static, o_ws = _both(cfg, None, dev)
+    assert torch.equal(o_static.view(torch.int16), o_ws.view(torch.int16))
+
+
 def test_noalloc_refuses_a_workspace_beyond_the_array():
     cfg = pxa.Config(32, 8, 32768, 128, 4, 0.95)              # needs about 73 MiB
     assert pxa.pxa_workspace_bytes(cfg) > pxa.PXA_NOALLOC_SCRATCH_BYTES
