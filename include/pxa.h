@@ -176,7 +176,7 @@ int pxa_prefill_ex(const pxa_config* cfg, const pxa_options* opts, const void* q
  * nothing.  It works on the current device (the stream must belong to it); its
  * first call on a device looks the array's address up.  PXA_EWORKSPACE, before
  * any device work, when pxa_workspace_bytes_ex(cfg, opts) exceeds the array
- * (64 MiB: e.g. 28,672 tokens of a 32-head, 8-KV-head, d = 128 layer with
+ * (64 MiB: up to 28,883 tokens of a 32-head, 8-KV-head, d = 128 layer with
  * four proxies).  Every call on one GPU shares that GPU's array, and the
  * array keeps the last call's intermediates (every one is written before it
  * is read, so nothing needs clearing): calls that overlap in time on one GPU,
