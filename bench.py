@@ -60,6 +60,9 @@ def parse():
                     help="skip the context timing of torch's flash SDPA at the same shape")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0,
                     help="approximate CPU seconds for the oracle sample")
+    ap.add_argument("--no-live-traffic", action="store_true",
+                    help="skip the two rocprofv3 counter passes that measure the sparse kernel's "
+                         "HBM traffic in this run (the committed profile is used instead)")
     ap.add_argument("--profile", action="store_true",
                     help="short pass for hardware counters: one 256 MiB device copy (counter "
                          "calibration), one warm pxa_prefill, then --steps passes of the stages")
@@ -107,6 +110,78 @@ def profiled_traffic(workload, config):
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _is_sparse_attention(kernel_name):
+    """fa_prefill_kernel<D, DENSE, SKIP> with DENSE false."""
+    tag = "fa_prefill_kernel<"
+    if tag not in kernel_name:
+        return False
+    args = kernel_name.split(tag, 1)[1].split(">", 1)[0].split(",")
+    return len(args) == 3 and args[1].strip() == "false"
+
+
+def live_traffic(a, timeout_s=180):
+    """HBM bytes per launch of the sparse attention kernel, measured in this run.
+
+    Two rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE) run a child
+    `bench.py --profile` of the same configuration. Each counter is averaged
+    over the kernel's launches and scaled by what it reads for the 256 MiB
+    device copy the child makes first (KiB per launch). Returns None if
+    rocprofv3 is missing or a pass fails or times out.
+    """
+    import csv
+    import glob
+    import shutil
+    import signal
+    import subprocess
+    import tempfile
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None
+    child = [sys.executable, os.path.abspath(__file__), "--workload", a.workload, "--profile",
+             "--steps", "1", "--budget", a.budget, "--score-stride", str(a.score_stride),
+             "--skip-threshold", repr(a.skip_threshold)]
+    if a.gamma is not None:
+        child += ["--gamma", repr(a.gamma)]
+    if a.seq_len is not None:
+        child += ["--seq-len", str(a.seq_len)]
+    env = dict(os.environ, TMPDIR="/tmp")
+    total = 0.0
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        log(f"counter pass {counter} (rocprofv3, child bench.py --profile)")
+        with tempfile.TemporaryDirectory(dir="/tmp") as d:
+            cmd = [prof, "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "p", "--"] + child
+            # the child's log lines go to this process's stderr; stdout stays the JSON line's
+            p = subprocess.Popen(cmd, cwd="/tmp", env=env, stdout=subprocess.DEVNULL,
+                                 start_new_session=True)
+            try:
+                p.wait(timeout=timeout_s)
+            except subprocess.TimeoutExpired:
+                os.killpg(p.pid, signal.SIGKILL)
+                p.wait()
+                log(f"counter pass {counter} timed out")
+                return None
+            # the profiler itself may end with an error after a complete run; the
+            # results file decides
+            files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+            if not files:
+                log(f"counter pass {counter}: no results (rc {p.returncode})")
+                return None
+            copy_kib, kernel_kib = None, []
+            with open(files[0]) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    if "copyBuffer" in r["Kernel_Name"] and copy_kib is None:
+                        copy_kib = float(r["Counter_Value"])
+                    elif _is_sparse_attention(r["Kernel_Name"]):
+                        kernel_kib.append(float(r["Counter_Value"]))
+            if not copy_kib or not kernel_kib:
+                log(f"counter pass {counter}: calibration or kernel rows missing")
+                return None
+            total += sum(kernel_kib) / len(kernel_kib) * 1024.0 * (262144.0 / copy_kib)
+    return total
 
 
 def cpu_baseline(cfg, x, samples, n_kept, gpu_csr, budget_s=20.0, last_blocks=1,
@@ -637,7 +712,15 @@ def main():
         "cpu_baseline": cpu,
         "host_wall_ms_per_step": round(wall_ms, 3),
     }
-    res["roofline"]["traffic"] = profiled_traffic(wl.name, res["config"])
+    traffic, source = None, None
+    if not a.no_live_traffic:
+        traffic = live_traffic(a)
+        source = "rocprofv3 FETCH_SIZE + WRITE_SIZE in this run" if traffic is not None else None
+    if traffic is None:
+        traffic = profiled_traffic(wl.name, res["config"])
+        source = (f"profiles/fa_prefill_sparse_{wl.name}.md" if traffic is not None else None)
+    res["roofline"]["traffic"] = round(traffic) if traffic is not None else None
+    res["roofline"]["traffic_source"] = source
     print(json.dumps(res), flush=True)
 
 

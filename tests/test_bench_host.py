@@ -76,3 +76,18 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+def test_sparse_attention_kernel_names_are_recognised():
+    assert bench._is_sparse_attention("void pxa::fa_prefill_kernel<128, false, false>(__bf16 const*)")
+    assert bench._is_sparse_attention("void pxa::fa_prefill_kernel<64, false, true>(x)")
+    assert not bench._is_sparse_attention("void pxa::fa_prefill_kernel<128, true, false>(x)")
+    assert not bench._is_sparse_attention("void pxa::proxy_score_kernel<128, 1, false>(x)")
+
+
+def test_live_traffic_is_null_without_the_profiler(monkeypatch):
+    import shutil
+    monkeypatch.setattr(shutil, "which", lambda name: None)
+    a = bench.argparse.Namespace(workload="w", budget="dynamic:1", score_stride=1, skip_threshold=0.0,
+                                 gamma=None, seq_len=None)
+    assert bench.live_traffic(a) is None
