@@ -262,3 +262,40 @@ def test_sparse_kernel_skips_invalid_entries_and_zeroes_empty_rows():
     # rows without the diagonal block: the first queries of the block still
     # see every key of the kept off-diagonal blocks, so outputs are defined
     assert_outputs_close(got, ref, "hand CSR")
+
+
+@pytest.mark.parametrize("name,a", [("d128_rope_13blk", 40), ("d128_rope_13blk", -50),
+                                    ("tiny_d64_2k", 60)])
+def test_power_of_two_rescaling_leaves_every_result_bit_identical(name, a):
+    """q * 2^a with k * 2^-a leaves every logit unchanged, and every step is
+    exact under that rescaling: the pooled means scale exactly, the block
+    exponents shift by a, the stored fp16 proxies, the scores, masses,
+    budgets, mask and outputs must not change by one bit.  It drives the
+    block-scaled proxies to extreme exponents (|a| up to 60)."""
+    wl, cfg, q, k, v, dev = case_data(name)
+    print(f"[rescale] {name} a={a}", flush=True)
+    scaled = dict(q=dev["q"] * (2.0 ** a), k=dev["k"] * (2.0 ** -a), v=dev["v"])
+    # the rescaling is exact in bf16 for these inputs (no overflow, no subnormals)
+    assert torch.equal((scaled["q"].float() * 2.0 ** -a).to(torch.bfloat16), dev["q"])
+    assert torch.equal((scaled["k"].float() * 2.0 ** a).to(torch.bfloat16), dev["k"])
+    runs = []
+    for inputs in (dev, scaled):
+        attn = pxa.ProxyAttn(cfg)
+        o = attn(inputs["q"], inputs["k"], inputs["v"])
+        torch.cuda.synchronize()
+        nnz = int(attn.row_ptr[-1])
+        runs.append(dict(o=o.clone(), qbar=attn.qbar.clone(), kbar=attn.kbar.clone(),
+                         qexp=attn.qexp.clone(), kexp=attn.kexp.clone(),
+                         scores=attn.scores.clone(), masses=attn.masses.clone(),
+                         k_h=attn.k_h.clone(), row_ptr=attn.row_ptr.clone(),
+                         col_idx=attn.col_idx[:nnz].clone()))
+    base, resc = runs
+    assert torch.equal(resc["qexp"], base["qexp"] - a)
+    assert torch.equal(resc["kexp"], base["kexp"] + a)
+    for key in ("qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx", "o"):
+        x, y = base[key], resc[key]
+        if x.dtype in (torch.float16, torch.bfloat16):
+            x, y = x.view(torch.int16), y.view(torch.int16)
+        elif x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        assert torch.equal(x, y), key
