@@ -264,20 +264,22 @@ def test_sparse_kernel_skips_invalid_entries_and_zeroes_empty_rows():
     assert_outputs_close(got, ref, "hand CSR")
 
 
-@pytest.mark.parametrize("name,a", [("d128_rope_13blk", 40), ("d128_rope_13blk", -50),
-                                    ("tiny_d64_2k", 60)])
-def test_power_of_two_rescaling_leaves_every_result_bit_identical(name, a):
+@pytest.mark.parametrize("name,a,b", [("d128_rope_13blk", 40, 0), ("d128_rope_13blk", -50, 20),
+                                      ("tiny_d64_2k", 60, -30)])
+def test_power_of_two_rescaling_leaves_every_result_bit_identical(name, a, b):
     """q * 2^a with k * 2^-a leaves every logit unchanged, and every step is
     exact under that rescaling: the pooled means scale exactly, the block
     exponents shift by a, the stored fp16 proxies, the scores, masses,
-    budgets, mask and outputs must not change by one bit.  It drives the
-    block-scaled proxies to extreme exponents (|a| up to 60)."""
+    budgets and mask must not change by one bit; v * 2^b scales every output
+    by exactly 2^b.  It drives the block-scaled proxies to extreme exponents
+    (|a| up to 60)."""
     wl, cfg, q, k, v, dev = case_data(name)
-    print(f"[rescale] {name} a={a}", flush=True)
-    scaled = dict(q=dev["q"] * (2.0 ** a), k=dev["k"] * (2.0 ** -a), v=dev["v"])
+    print(f"[rescale] {name} a={a} b={b}", flush=True)
+    scaled = dict(q=dev["q"] * (2.0 ** a), k=dev["k"] * (2.0 ** -a), v=dev["v"] * (2.0 ** b))
     # the rescaling is exact in bf16 for these inputs (no overflow, no subnormals)
     assert torch.equal((scaled["q"].float() * 2.0 ** -a).to(torch.bfloat16), dev["q"])
     assert torch.equal((scaled["k"].float() * 2.0 ** a).to(torch.bfloat16), dev["k"])
+    assert torch.equal((scaled["v"].float() * 2.0 ** -b).to(torch.bfloat16), dev["v"])
     runs = []
     for inputs in (dev, scaled):
         attn = pxa.ProxyAttn(cfg)
@@ -292,6 +294,7 @@ def test_power_of_two_rescaling_leaves_every_result_bit_identical(name, a):
     base, resc = runs
     assert torch.equal(resc["qexp"], base["qexp"] - a)
     assert torch.equal(resc["kexp"], base["kexp"] + a)
+    resc["o"] = (resc["o"].float() * 2.0 ** -b).to(torch.bfloat16)
     for key in ("qbar", "kbar", "scores", "masses", "k_h", "row_ptr", "col_idx", "o"):
         x, y = base[key], resc[key]
         if x.dtype in (torch.float16, torch.bfloat16):
